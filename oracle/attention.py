@@ -1,0 +1,257 @@
+"""fp64 CPU oracle for the FlashAttention forward pass and its split-KV decode.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or
+execute this module: only the tests under ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` use it. It shares no code with the
+HIP library and imports nothing from it.
+
+Every function here is plain numpy in float64. Inputs are widened exactly from
+whatever the GPU consumed (bf16 or fp32 values are representable in fp64).
+
+Sources (the web pages the method is defined on):
+
+* "11. Fusion, recompute, and flash attention" (ML compiler from scratch),
+  section 11.2 (S = QK^T/sqrt(D), P = softmax(S) row-wise, O = PV), section 11.6
+  (online softmax per key and the merge of two partial states), section 11.9
+  (log-sum-exp m + log l saved per row), Pitfalls (fully masked rows),
+  Exercise "Causal mask" (query i attends keys j <= i), Exercise
+  "Flash-decoding" (split keys into chunks, merge partials in a second step),
+  Solutions to exercise 3 (the merge worked with numbers).
+* iThome article on FlashAttention (ithelp.ithome.com.tw/articles/10405336),
+  sections on standard attention, stable softmax and "the three states"
+  (m, l, O with alpha = exp(m - m_new), final O / l).
+* "Kernel visualization: Flash Attention 2", section "Write the data back to
+  HBM" (L = m + log l written beside O).
+* phobos attention stdlib page, ``attention`` (mask of the ragged last key
+  block) and ``Causal attention``.
+
+What pins each function (tests/test_oracle.py):
+
+* ``attention``: closed forms (Nk = 1; K = 0 gives prefix means with
+  LSE = ln(count)), invariants (weights sum to one, V = 1 gives O = 1, joint
+  K/V row permutation, causal row 0 = V[0], causal last row = full last row),
+  torch's float64 CPU ``scaled_dot_product_attention`` and ``logsumexp`` as an
+  independent library routine, and agreement with ``online_blocked``.
+* ``online_per_key``: the worked example of section 11.6 (state after every key
+  and o/l = 21.546979), checked against tests/golden/worked_example.json.
+* ``online_blocked``: agreement with ``attention`` on tiny inputs for block
+  sizes that do and do not divide Nk; the late-maximum case of the exercise
+  "Find the bug".
+* ``merge`` / ``split_states`` / ``combine``: the numbers of the solution to
+  exercise 3 (tests/golden/merge_example.json); every chunking of a row gives
+  the two-pass answer.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+NEG_INF = -math.inf
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def allowed_keys(i: int, nk: int, causal: bool) -> np.ndarray:
+    """Boolean mask of the keys query row ``i`` may attend.
+
+    Keys are 0..nk-1. With ``causal`` the row attends only keys j <= i,
+    counted from the first key (top-left alignment: the exercise "Causal mask"
+    defines it on square inputs, and the same absolute rule is kept when
+    Nq != Nk).
+    """
+    j = np.arange(nk)
+    if causal:
+        return j <= i
+    return np.ones(nk, dtype=bool)
+
+
+def attention_rows(q_rows, row_index, k, v, scale: float, causal: bool):
+    """Two-pass attention for selected query rows of one (batch, head).
+
+    q_rows: [R, D] queries; row_index: [R] their absolute row numbers (used by
+    the causal mask); k, v: [Nk, D]. Returns (O [R, D], LSE [R]).
+
+    Follows section 11.2 and the stable softmax of the iThome article: the
+    score row s = scale * q . k_j is materialised, m = max over the allowed
+    keys, p = exp(s - m), l = sum p, O = (sum_j p_j v_j) / l. LSE = m + ln l
+    on the scaled scores, as the write-back step of the FA2 visualization
+    stores it.
+    """
+    q_rows, k, v = _f64(q_rows), _f64(k), _f64(v)
+    nk = k.shape[0]
+    s = scale * (q_rows @ k.T)                       # [R, Nk]
+    mask = np.stack([allowed_keys(int(i), nk, causal) for i in row_index])
+    s = np.where(mask, s, NEG_INF)
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)                                 # exp(-inf) = 0 for masked keys
+    l = p.sum(axis=1, keepdims=True)
+    o = (p @ v) / l
+    lse = m[:, 0] + np.log(l[:, 0])
+    return o, lse
+
+
+def attention(q, k, v, scale: float, causal: bool = False):
+    """softmax(Q K^T * scale) V over tensors laid out [B, H, N, D].
+
+    q: [B, H, Nq, D]; k, v: [B, H, Nk, D]. Returns O [B, H, Nq, D] and
+    LSE [B, H, Nq] in float64. This is the definition the method reaches
+    exactly (the iThome article calls FlashAttention exact attention): every
+    row is computed in two passes by ``attention_rows``.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    b, h, nq, d = q.shape
+    o = np.empty((b, h, nq, v.shape[-1]))
+    lse = np.empty((b, h, nq))
+    rows = np.arange(nq)
+    for bi in range(b):
+        for hi in range(h):
+            o[bi, hi], lse[bi, hi] = attention_rows(q[bi, hi], rows, k[bi, hi], v[bi, hi], scale, causal)
+    return o, lse
+
+
+def softmax_weights(q, k, scale: float, causal: bool = False):
+    """The probability matrix P = softmax(scale * Q K^T) of one (batch, head).
+
+    q: [Nq, D], k: [Nk, D] -> P [Nq, Nk]; masked entries are exactly 0.
+    Exposed so tests can check that every row sums to one.
+    """
+    q, k = _f64(q), _f64(k)
+    nk = k.shape[0]
+    s = scale * (q @ k.T)
+    mask = np.stack([allowed_keys(i, nk, causal) for i in range(q.shape[0])])
+    s = np.where(mask, s, NEG_INF)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    return p / p.sum(axis=1, keepdims=True)
+
+
+# --------------------------------------------------------------------------
+# Online softmax: the recurrence the kernels implement, kept here only so the
+# tests can check it against the two-pass definition above.
+# --------------------------------------------------------------------------
+
+def online_per_key(s, v, trace: bool = False):
+    """Online softmax over one score row, one key at a time (section 11.6).
+
+    s: [N] scaled scores; v: [N, Dv] (or [N] for a scalar value). State starts
+    at (m, l, o) = (-inf, 0, 0). For each key j the maximum becomes
+    m_j = max(m_{j-1}, s_j), the old sum and output are multiplied by
+    corr = exp(m_{j-1} - m_j) and the key adds exp(s_j - m_j) (times v_j).
+    Returns (m, l, o) and, with ``trace``, the list of per-key states
+    (m, corr, p, l, o). The answer is o / l.
+    """
+    s = _f64(s)
+    v = _f64(v)
+    o = np.zeros(v.shape[1:])
+    m, l = NEG_INF, 0.0
+    states = []
+    for j in range(s.shape[0]):
+        m_new = max(m, s[j])
+        # exp(-inf - finite) = 0 multiplies the empty start state; a row whose
+        # every score so far is -inf keeps corr = 1 instead of exp(nan).
+        corr = 1.0 if m_new == NEG_INF else math.exp(m - m_new)
+        p = 0.0 if m_new == NEG_INF else math.exp(s[j] - m_new)
+        l = l * corr + p
+        o = o * corr + p * v[j]
+        m = m_new
+        if trace:
+            states.append((m, corr, p, l, np.array(o)))
+    if trace:
+        return (m, l, o), states
+    return m, l, o
+
+
+def online_blocked(q, k, v, scale: float, causal: bool, block: int):
+    """Block-wise online softmax over keys (the FA2 form of the iThome article).
+
+    For each query row of one (batch, head) and each block of ``block`` keys:
+    S_blk = scale * q K_blk^T with masked keys at -inf, m_new = max(m, max S_blk),
+    alpha = exp(m - m_new), P = exp(S_blk - m_new), l = alpha l + sum P,
+    O = alpha O + P V_blk, m = m_new; after the last block O / l and
+    LSE = m + ln l. A block may hold fewer than ``block`` keys at the end
+    (the masked last block of the phobos ``attention``). Plain loops: tiny
+    inputs only.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    nq, nk = q.shape[0], k.shape[0]
+    out = np.zeros((nq, v.shape[1]))
+    lse = np.zeros(nq)
+    for i in range(nq):
+        ok = allowed_keys(i, nk, causal)
+        m, l = NEG_INF, 0.0
+        acc = np.zeros(v.shape[1])
+        for j0 in range(0, nk, block):
+            j1 = min(nk, j0 + block)
+            s = scale * (k[j0:j1] @ q[i])
+            s = np.where(ok[j0:j1], s, NEG_INF)
+            m_new = max(m, float(s.max()))
+            if m_new == NEG_INF:          # nothing allowed yet: state stays empty
+                continue
+            alpha = math.exp(m - m_new)
+            p = np.exp(s - m_new)
+            l = alpha * l + p.sum()
+            acc = alpha * acc + p @ v[j0:j1]
+            m = m_new
+        out[i] = acc / l
+        lse[i] = m + math.log(l)
+    return out, lse
+
+
+def merge(a, b):
+    """Merge two partial states (m, l, o) into the state of the union of their keys.
+
+    With m = max(m1, m2): l = l1 e^{m1-m} + l2 e^{m2-m}, o = o1 e^{m1-m} + o2 e^{m2-m}
+    (section 11.6, proved in the solution to exercise 3). An empty state
+    (-inf, 0, 0) is the identity.
+    """
+    m1, l1, o1 = a
+    m2, l2, o2 = b
+    m = max(m1, m2)
+    if m == NEG_INF:
+        return (NEG_INF, 0.0, np.zeros_like(_f64(o1)))
+    w1 = math.exp(m1 - m)
+    w2 = math.exp(m2 - m)
+    return (m, l1 * w1 + l2 * w2, _f64(o1) * w1 + _f64(o2) * w2)
+
+
+def chunk_bounds(nk: int, num_splits: int):
+    """Key ranges of the split-KV decode: chunk c = ceil(nk / num_splits) keys,
+    chunk s covers [s*c, min(nk, (s+1)*c)); trailing chunks may be empty."""
+    c = -(-nk // num_splits)
+    return [(min(nk, s * c), min(nk, (s + 1) * c)) for s in range(num_splits)]
+
+
+def split_states(q_row, k, v, scale: float, num_splits: int):
+    """Partial (m, l, o) of one query row over each key chunk (exercise
+    "Flash-decoding"): each chunk is reduced in two passes on its own keys.
+    Empty chunks give (-inf, 0, 0)."""
+    q_row, k, v = _f64(q_row), _f64(k), _f64(v)
+    parts = []
+    for j0, j1 in chunk_bounds(k.shape[0], num_splits):
+        if j1 <= j0:
+            parts.append((NEG_INF, 0.0, np.zeros(v.shape[1])))
+            continue
+        s = scale * (k[j0:j1] @ q_row)
+        m = float(s.max())
+        p = np.exp(s - m)
+        parts.append((m, float(p.sum()), p @ v[j0:j1]))
+    return parts
+
+
+def combine(parts):
+    """Fold a list of partial states with ``merge`` and finish: (o / l, m + ln l)."""
+    state = (NEG_INF, 0.0, np.zeros_like(_f64(parts[0][2])))
+    for p in parts:
+        state = merge(state, p)
+    m, l, o = state
+    return o / l, m + math.log(l)
+
+
+def decode(q, k, v, scale: float):
+    """Single-token decode: q [B, H, 1, D] over the whole cache k, v [B, H, Nk, D],
+    no mask. The same definition as ``attention`` with Nq = 1; returns
+    O [B, H, 1, D] and LSE [B, H, 1]."""
+    return attention(q, k, v, scale, causal=False)

@@ -1,0 +1,258 @@
+"""Pins that tie the fp64 oracle to facts fixed by the pages and by mathematics.
+
+Each ``pin_*`` takes the oracle module as its argument so the same checks can be
+run on deliberately broken copies of the oracle (tests/test_oracle_mutations.py)
+to show that a plausible mistake is caught. None of these re-types the oracle's
+own formula: they use printed numbers, closed forms, invariants, an independent
+library routine (torch's float64 CPU attention) or a different algorithm
+(online recurrences against the two-pass definition).
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _close(a, b, tol, what):
+    a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= tol, f"{what}: max abs err {err:.3e} > {tol:.1e}"
+
+
+# ---- printed worked examples -------------------------------------------------
+
+def pin_worked_example_trace(orc):
+    """Online softmax state after every key equals the printed trace (section 11.6)."""
+    g = _golden("worked_example.json")
+    (m, l, o), states = orc.online_per_key(g["scores"], g["values"], trace=True)
+    half_ulp = 0.5 * 10.0 ** (-g["printed_decimals"]) + 1e-12
+    assert len(states) == len(g["states"])
+    for got, want in zip(states, g["states"]):
+        for idx, key in enumerate(["m", "corr", "p", "l", "o"]):
+            _close(got[idx], want[key], half_ulp, f"key {want['key']} {key}")
+    _close(o / l, g["o_over_l"], 0.5 * 10.0 ** (-g["o_over_l_decimals"]) + 1e-12, "online o/l")
+
+
+def pin_worked_example_two_pass(orc):
+    """The two-pass definition gives the printed 21.546979 and LSE = 3 + ln(1 + e^-1 + e^-2)."""
+    g = _golden("worked_example.json")
+    q = np.ones((1, 1, 1, 1))
+    k = np.array(g["scores"]).reshape(1, 1, 3, 1)
+    v = np.array(g["values"]).reshape(1, 1, 3, 1)
+    o, lse = orc.attention(q, k, v, 1.0, causal=False)
+    _close(o[0, 0, 0, 0], g["o_over_l"], 0.5e-6 + 1e-12, "two-pass o")
+    _close(lse[0, 0, 0], 3.0 + math.log(1.0 + math.exp(-1.0) + math.exp(-2.0)), 1e-14, "two-pass lse")
+
+
+def pin_merge_example(orc):
+    """Solution 3: states of {0} and {1, 2} and their merge, as printed."""
+    g = _golden("merge_example.json")
+    s, v = g["scores"], g["values"]
+    tol = 0.5 * 10.0 ** (-g["printed_decimals"]) + 1e-12
+    a = orc.online_per_key(s[:1], v[:1])
+    b = orc.online_per_key(s[1:], v[1:])
+    for state, want, what in [(a, g["part_a"], "{0}"), (b, g["part_b"], "{1,2}")]:
+        _close(state[0], want["m"], tol, what + " m")
+        _close(state[1], want["l"], tol, what + " l")
+        _close(state[2], want["o"], tol, what + " o")
+    mm, ml, mo = orc.merge(a, b)
+    _close(mm, g["merged"]["m"], tol, "merged m")
+    _close(ml, g["merged"]["l"], tol, "merged l")
+    _close(mo, g["merged"]["o"], tol, "merged o")
+    o, _ = orc.combine([a, b])
+    _close(o, g["o_over_l"], 0.5 * 10.0 ** (-g["o_over_l_decimals"]) + 1e-12, "merged o/l")
+
+
+# ---- closed forms ------------------------------------------------------------
+
+def pin_single_key(orc):
+    """Nk = 1: O = V[0] and LSE = scale * q . k_0 for every row, causal or not."""
+    q = _rand((2, 3, 5, 8), 1)
+    k = _rand((2, 3, 1, 8), 2)
+    v = _rand((2, 3, 1, 8), 3)
+    scale = 0.37
+    for causal in (False, True):
+        o, lse = orc.attention(q, k, v, scale, causal)
+        _close(o, np.broadcast_to(v, o.shape), 1e-14, "Nk=1 O")
+        _close(lse, scale * np.einsum("bhnd,bhd->bhn", q, k[:, :, 0]), 1e-13, "Nk=1 LSE")
+
+
+def pin_zero_keys_means(orc):
+    """K = 0: every allowed key has weight 1/count, so O is a mean of V rows and
+    LSE = ln(count). Causal row i averages V[0..i] (prefix means)."""
+    nq = nk = 9
+    q = _rand((1, 2, nq, 4), 4)
+    k = np.zeros((1, 2, nk, 4))
+    v = _rand((1, 2, nk, 4), 5)
+    o, lse = orc.attention(q, k, v, 0.5, causal=False)
+    _close(o, np.broadcast_to(v.mean(axis=2, keepdims=True), o.shape), 1e-14, "K=0 full O")
+    _close(lse, np.full(lse.shape, math.log(nk)), 1e-14, "K=0 full LSE")
+    o, lse = orc.attention(q, k, v, 0.5, causal=True)
+    prefix = np.cumsum(v, axis=2) / np.arange(1, nk + 1)[None, None, :, None]
+    _close(o, prefix, 1e-14, "K=0 causal O")
+    _close(lse, np.broadcast_to(np.log(np.arange(1, nq + 1)), lse.shape), 1e-14, "K=0 causal LSE")
+
+
+def pin_zero_scale_rectangular(orc):
+    """scale = 0 with Nq != Nk: non-causal rows are column means; causal row i
+    (top-left) averages V[0..min(i, Nk-1)]."""
+    nq, nk = 7, 4
+    q = _rand((1, 1, nq, 3), 6)
+    k = _rand((1, 1, nk, 3), 7)
+    v = _rand((1, 1, nk, 3), 8)
+    o, _ = orc.attention(q, k, v, 0.0, causal=True)
+    for i in range(nq):
+        _close(o[0, 0, i], v[0, 0, : min(i, nk - 1) + 1].mean(axis=0), 1e-14, f"scale=0 causal row {i}")
+    o, _ = orc.attention(q, k, v, 0.0, causal=False)
+    _close(o[0, 0], np.broadcast_to(v[0, 0].mean(axis=0), (nq, 3)), 1e-14, "scale=0 full")
+
+
+# ---- invariants --------------------------------------------------------------
+
+def pin_weights_sum_to_one(orc):
+    q = _rand((13, 6), 9)
+    k = _rand((11, 6), 10) * 4.0
+    for causal in (False, True):
+        p = orc.softmax_weights(q, k, 0.41, causal)
+        _close(p.sum(axis=1), np.ones(13), 1e-14, "row sums")
+        assert np.all(p >= 0.0)
+        if causal:
+            assert np.all(p[np.triu_indices(11, 1)] == 0.0), "masked weight not zero"
+
+
+def pin_ones_values(orc):
+    q = _rand((1, 2, 10, 5), 11) * 3.0
+    k = _rand((1, 2, 10, 5), 12) * 3.0
+    v = np.ones((1, 2, 10, 5))
+    for causal in (False, True):
+        o, _ = orc.attention(q, k, v, 0.3, causal)
+        _close(o, np.ones_like(o), 1e-14, "V=1")
+
+
+def pin_permutation(orc):
+    """Permuting K and V rows together leaves non-causal O and LSE unchanged."""
+    q = _rand((2, 1, 6, 7), 13)
+    k = _rand((2, 1, 12, 7), 14)
+    v = _rand((2, 1, 12, 7), 15)
+    perm = np.random.default_rng(16).permutation(12)
+    o1, l1 = orc.attention(q, k, v, 0.5)
+    o2, l2 = orc.attention(q, k[:, :, perm], v[:, :, perm], 0.5)
+    _close(o1, o2, 1e-13, "permuted O")
+    _close(l1, l2, 1e-13, "permuted LSE")
+
+
+def pin_causal_edges(orc):
+    """Causal row 0 is V[0] exactly; the last row of a square causal problem sees
+    every key and equals the non-causal last row exactly."""
+    q = _rand((1, 3, 8, 4), 17) * 2.0
+    k = _rand((1, 3, 8, 4), 18) * 2.0
+    v = _rand((1, 3, 8, 4), 19)
+    oc, lc = orc.attention(q, k, v, 0.7, causal=True)
+    of, lf = orc.attention(q, k, v, 0.7, causal=False)
+    assert np.array_equal(oc[:, :, 0], v[:, :, 0]), "causal row 0 != V[0]"
+    _close(lc[:, :, 0], 0.7 * np.einsum("bhd,bhd->bh", q[:, :, 0], k[:, :, 0]), 1e-14, "causal row 0 LSE")
+    assert np.array_equal(oc[:, :, -1], of[:, :, -1]), "causal last row != full last row"
+    assert np.array_equal(lc[:, :, -1], lf[:, :, -1])
+    assert not np.allclose(oc[:, :, 1:-1], of[:, :, 1:-1]), "causal mask had no effect"
+
+
+# ---- an independent library routine -----------------------------------------
+
+def pin_torch_sdpa(orc):
+    """torch's float64 CPU scaled_dot_product_attention (top-left causal mask)
+    and logsumexp agree with the oracle."""
+    for (b, h, nq, nk, d, causal, seed) in [(2, 3, 17, 17, 8, False, 20), (1, 2, 19, 19, 16, True, 21),
+                                            (1, 1, 5, 23, 4, False, 22), (1, 2, 23, 9, 4, True, 23)]:
+        q = _rand((b, h, nq, d), seed) * 2.0
+        k = _rand((b, h, nk, d), seed + 100) * 2.0
+        v = _rand((b, h, nk, d), seed + 200)
+        scale = 1.0 / math.sqrt(d)
+        o, lse = orc.attention(q, k, v, scale, causal)
+        tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale)
+        _close(o, ref.numpy(), 1e-12, f"sdpa O {nq}x{nk} causal={causal}")
+        s = scale * (tq @ tk.transpose(-1, -2))
+        if causal:
+            s = s.masked_fill(~torch.ones(nq, nk, dtype=torch.bool).tril(), -math.inf)
+        _close(lse, torch.logsumexp(s, dim=-1).numpy(), 1e-12, f"logsumexp {nq}x{nk} causal={causal}")
+
+
+# ---- a different algorithm reaching the same result ---------------------------
+
+def pin_online_blocked_matches(orc):
+    """Block-wise online softmax = two-pass, for block sizes that do and do not
+    divide Nk, causal and not, and Nq != Nk."""
+    for (nq, nk, causal) in [(9, 9, True), (9, 9, False), (5, 13, False), (13, 13, True), (4, 11, True)]:
+        q = _rand((nq, 6), nq * 31 + nk) * 3.0
+        k = _rand((nk, 6), nq * 37 + nk) * 3.0
+        v = _rand((nk, 6), nq * 41 + nk)
+        o_ref, l_ref = orc.attention(q[None, None], k[None, None], v[None, None], 0.45, causal)
+        for block in (1, 2, 3, 4, 7, 16, nk + 5):
+            o, l = orc.online_blocked(q, k, v, 0.45, causal, block)
+            _close(o, o_ref[0, 0], 1e-12, f"blocked O block={block} causal={causal}")
+            _close(l, l_ref[0, 0], 1e-12, f"blocked LSE block={block} causal={causal}")
+
+
+def pin_online_per_key_matches(orc):
+    """Per-key recurrence = two-pass on a row whose maximum comes last (the case
+    of the exercise 'Find the bug')."""
+    s = np.array([0.5, -1.0, 2.0, 1.5, 9.0])
+    v = _rand((5, 3), 24)
+    m, l, o = orc.online_per_key(s, v)
+    q = np.ones((1, 1, 1, 1))
+    o_ref, l_ref = orc.attention(q, s.reshape(1, 1, 5, 1), v[None, None], 1.0)
+    _close(o / l, o_ref[0, 0, 0], 1e-14, "per-key late max")
+    _close(m + math.log(l), l_ref[0, 0, 0], 1e-14, "per-key LSE")
+
+
+def pin_split_combine(orc):
+    """Every chunking of the keys (including empty trailing chunks) merges back
+    to the two-pass answer (exercise 'Flash-decoding' with the merge rule)."""
+    nk = 37
+    q = _rand((1, 1, 1, 8), 25) * 2.0
+    k = _rand((1, 1, nk, 8), 26) * 2.0
+    v = _rand((1, 1, nk, 8), 27)
+    o_ref, l_ref = orc.decode(q, k, v, 0.35)
+    for splits in (1, 2, 3, 5, 8, nk, nk + 3, 64):
+        bounds = orc.chunk_bounds(nk, splits)
+        covered = np.concatenate([np.arange(a, b) for a, b in bounds])
+        assert np.array_equal(covered, np.arange(nk)), f"chunks do not tile the keys for S={splits}"
+        parts = orc.split_states(q[0, 0, 0], k[0, 0], v[0, 0], 0.35, splits)
+        o, lse = orc.combine(parts)
+        _close(o, o_ref[0, 0, 0], 1e-13, f"split O S={splits}")
+        _close(lse, l_ref[0, 0, 0], 1e-13, f"split LSE S={splits}")
+
+
+ALL_PINS = [
+    pin_worked_example_trace,
+    pin_worked_example_two_pass,
+    pin_merge_example,
+    pin_single_key,
+    pin_zero_keys_means,
+    pin_zero_scale_rectangular,
+    pin_weights_sum_to_one,
+    pin_ones_values,
+    pin_permutation,
+    pin_causal_edges,
+    pin_torch_sdpa,
+    pin_online_blocked_matches,
+    pin_online_per_key_matches,
+    pin_split_combine,
+]

@@ -1,0 +1,49 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and check that
+the pins catch every one of them."""
+
+import os
+import types
+
+import pytest
+
+from tests.oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "attention.py")
+
+MUTATIONS = {
+    "causal_off_by_one": ("return j <= i", "return j < i"),
+    "dropped_scale": ("s = scale * (q_rows @ k.T)", "s = (q_rows @ k.T)"),
+    "lse_without_max": ("lse = m[:, 0] + np.log(l[:, 0])", "lse = np.log(l[:, 0])"),
+    "lse_base_two": ("lse = m[:, 0] + np.log(l[:, 0])", "lse = m[:, 0] + np.log2(l[:, 0])"),
+    "no_final_divide": ("o = (p @ v) / l", "o = (p @ v)"),
+    "wrong_operand": ("o = (p @ v) / l", "o = (p @ k) / l"),
+    "unshifted_exp": ("p = np.exp(s - m)                                 #", "p = np.exp(s)                                     #"),
+    "per_key_forgot_rescale": ("o = o * corr + p * v[j]", "o = o + p * v[j]"),
+    "per_key_l_not_rescaled": ("l = l * corr + p", "l = l + p"),
+    "blocked_forgot_rescale": ("acc = alpha * acc + p @ v[j0:j1]", "acc = acc + p @ v[j0:j1]"),
+    "blocked_alpha_sign": ("alpha = math.exp(m - m_new)", "alpha = math.exp(m_new - m)"),
+    "merge_weight_sign": ("w1 = math.exp(m1 - m)", "w1 = math.exp(m - m1)"),
+    "merge_drops_second_o": ("o1) * w1 + _f64(o2) * w2)", "o1) * w1)"),
+    "chunk_floor": ("c = -(-nk // num_splits)", "c = max(1, nk // num_splits)"),
+}
+
+
+def _mutant(old, new):
+    with open(SRC) as f:
+        text = f.read()
+    assert text.count(old) == 1, f"mutation anchor not unique/present: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(text.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_mutation(name):
+    mod = _mutant(*MUTATIONS[name])
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(mod)
+        except Exception as e:  # noqa: BLE001 - any failure counts as caught
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin caught the planted mistake {name}"
