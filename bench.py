@@ -1,0 +1,223 @@
+"""Benchmark of the MI355X FlashAttention forward library.
+
+One step = one ``fa_forward`` call over the prefill workload the metric is
+quoted on (B=1, H=32, Nq=Nk=2048, D=128, bf16, non-causal), inputs already
+resident in HBM. The metric's second half, split-KV decode bandwidth, is
+measured in the same run on the decode workload (B=16, H=32, one query,
+Nk=32768, D=128, 64 splits) and reported under "decode". Prints ONE JSON line.
+
+Timing: W untimed warm-up steps, then K steps between two HIP events recorded
+on the stream the kernels are launched on (torch's current stream, which is
+the stream handed to the library), synchronised on both sides.
+
+Algorithmic counts (not the implementation's):
+  prefill FLOPs = 4*B*H*Nq*Nk*D (halved when causal)
+  bytes         = Q, K, V read once + O written once (+ LSE, fp32)
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s & % bf16 MFMA peak (prefill); decode GB/s & % HBM peak"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "flashattention_online_softmax_forward_amd", "csrc")
+
+
+def kernel_source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name, digest):
+    """HBM bytes per launch recorded from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+    in profiles/<name>.md, or None when absent or taken on other kernel source."""
+    path = os.path.join(PROFILES, name + ".md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"kernel_source_digest:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_src or not m_b or m_src.group(1) != digest:
+        return None
+    return float(m_b.group(1))
+
+
+def workload_counts(w):
+    flops = 4.0 * w.B * w.H * w.Nq * w.Nk * w.D * (0.5 if w.causal else 1.0)
+    elem = 4 if w.dtype.is_floating_point and w.dtype.itemsize == 4 else 2
+    bytes_ = elem * w.B * w.H * (2 * w.Nq * w.D + 2 * w.Nk * w.D) + 4 * w.B * w.H * w.Nq
+    return flops, bytes_
+
+
+def time_steps(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def cpu_baseline(w, q, k, v, budget_s):
+    """The fp64 oracle as it stands, on the host, over whole heads of the same
+    workload until about ``budget_s`` seconds of work are done."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention as orc
+
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    flops_head = 4.0 * w.Nq * w.Nk * w.D * (0.5 if w.causal else 1.0)
+    done, t_total = 0, 0.0
+    for (b, h) in heads:
+        qh = q[b, h].float().cpu().numpy().astype(np.float64)[None, None]
+        kh = k[b, h].float().cpu().numpy().astype(np.float64)[None, None]
+        vh = v[b, h].float().cpu().numpy().astype(np.float64)[None, None]
+        t0 = time.perf_counter()
+        orc.attention(qh, kh, vh, w.scale, w.causal)
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total >= budget_s:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {
+        "value": flops_head * done / t_total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} of {len(heads)} heads of {w.name} (fp64 two-pass, every row), {t_total:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill_b1_h32_n2048_d128")
+    ap.add_argument("--decode-workload", default="decode_b16_h32_kv32768_d128_s64")
+    ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead of attention, time a plain device copy of this many bytes "
+                         "(calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import flashattention_online_softmax_forward_amd as fa
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+
+    if args.copy_bytes:
+        n = args.copy_bytes // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        ms = time_steps(lambda: dst.copy_(src), args.steps, args.warmup, torch)
+        print(json.dumps({"copy_bytes": n * 4, "ms": ms, "GB/s": 2 * n * 4 / ms / 1e6}))
+        return
+
+    w = synth.WORKLOADS[args.workload]
+    q, k, v = synth.make_workload(w, seed=0, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+    if w.is_decode:
+        raise SystemExit("--workload names a prefill workload; decode is reported under 'decode'")
+    if w.dtype == torch.float32:
+        step = lambda: fa.fa_forward_f32(q, k, v, causal=w.causal, scale=w.scale, out=out, lse=lse)  # noqa: E731
+        peak, dtype, kname = PEAK_FP32_TFLOPS, "f32", "fwd_f32_kernel"
+        files = ["fa_fwd_f32.hip", "fa_device.h", "fa_internal.h"]
+    else:
+        step = lambda: fa.fa_forward(q, k, v, causal=w.causal, scale=w.scale, out=out, lse=lse)  # noqa: E731
+        peak, dtype, kname = PEAK_BF16_TFLOPS, "bf16", "fwd_bf16_kernel"
+        files = ["fa_fwd_bf16.hip", "fa_device.h", "fa_internal.h"]
+    ms = time_steps(step, args.steps, args.warmup, torch)
+    flops, _ = workload_counts(w)
+    tflops = flops / (ms * 1e-3) / 1e12
+    digest = kernel_source_digest(files)
+    traffic = measured_traffic(f"{kname}_{w.name}", digest)
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded i.i.d. N(0,1) inputs)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "D": w.D,
+                   "causal": w.causal, "scale": w.scale},
+        "roofline": {"kernel": kname, "bound": "mfma", "achieved": round(tflops, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic,
+                     "kernel_source_digest": digest},
+    }
+
+    if not args.no_decode:
+        dw = synth.WORKLOADS[args.decode_workload]
+        dq, dk, dv = synth.make_workload(dw, seed=0, device="cuda")
+        dout = torch.empty_like(dq)
+        dlse = torch.empty((dw.B, dw.H), dtype=torch.float32, device="cuda")
+        ws = torch.empty(fa.fa_decode_workspace_bytes(dw.B, dw.H, dw.D, dw.num_splits), dtype=torch.uint8,
+                         device="cuda")
+        dstep = lambda: fa.fa_decode_splitkv(dq, dk, dv, dw.num_splits, scale=dw.scale, workspace=ws,  # noqa: E731
+                                             out=dout, lse=dlse)
+        dms = time_steps(dstep, args.decode_steps, args.warmup, torch)
+        _, dbytes = workload_counts(dw)
+        gbs = dbytes / (dms * 1e-3) / 1e9
+        ddigest = kernel_source_digest(["fa_decode.hip", "fa_device.h", "fa_internal.h"])
+        result["decode"] = {
+            "workload": dw.name, "ms_per_call": round(dms, 6), "value": round(gbs, 2), "unit": "GB/s",
+            "algorithmic_bytes": dbytes, "num_splits": dw.num_splits,
+            "roofline": {"kernel": "decode_partial_kernel + decode_combine_kernel", "bound": "hbm",
+                         "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic(f"decode_partial_kernel_{dw.name}", ddigest),
+                         "kernel_source_digest": ddigest},
+        }
+        del dq, dk, dv, ws
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,137 @@
+"""MI355X (gfx950) FlashAttention forward: thin Python binding of include/fa.h.
+
+Each function marshals torch tensors into the C ABI of ``libfa_mi355x.so`` and
+nothing else: every step of the computation runs in the library's HIP kernels.
+torch supplies device memory and the current stream. Tensors are [B, H, N, D]
+contiguous on a ROCm device; outputs are allocated here with torch when the
+caller does not pass them. There is no CPU fallback: without the built library
+or a GPU tensor these functions raise.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+__all__ = [
+    "fa_forward",
+    "fa_forward_f32",
+    "fa_decode_splitkv",
+    "fa_decode_workspace_bytes",
+    "fa_status_string",
+    "FAError",
+]
+
+FAError = _lib.FAError
+
+
+def fa_status_string(code: int) -> str:
+    return _lib.status_string(code)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _check_tensor(name: str, t: torch.Tensor, dtype: torch.dtype, ndim: int = 4) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on a ROCm GPU (got {t.device}); there is no CPU path")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D [B, H, N, D] (got shape {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _forward(fn_name, dtype, q, k, v, causal, scale, out, lse, want_lse):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, dtype)
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    if tuple(k.shape) != (B, H, Nk, D) or tuple(v.shape) != (B, H, Nk, D):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor("out", out, dtype)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_tensor("lse", lse, torch.float32, ndim=3)
+        if tuple(lse.shape) != (B, H, Nq):
+            raise ValueError("lse must be [B, H, Nq]")
+    fn = getattr(_lib.load(), fn_name)
+    code = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+              lse.data_ptr() if lse is not None else None,
+              B, H, Nq, Nk, D, float(scale), int(bool(causal)), _stream(q))
+    _lib.check(code, fn_name)
+    return out, lse
+
+
+def fa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+               scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+               lse: Optional[torch.Tensor] = None, want_lse: bool = True
+               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """bf16 forward: returns (O bf16 [B,H,Nq,D], LSE fp32 [B,H,Nq] or None)."""
+    return _forward("fa_forward", torch.bfloat16, q, k, v, causal, scale, out, lse, want_lse)
+
+
+def fa_forward_f32(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                   scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, want_lse: bool = True
+                   ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """fp32 forward: returns (O fp32 [B,H,Nq,D], LSE fp32 [B,H,Nq] or None)."""
+    return _forward("fa_forward_f32", torch.float32, q, k, v, causal, scale, out, lse, want_lse)
+
+
+def fa_decode_workspace_bytes(B: int, H: int, D: int, num_splits: int) -> int:
+    return int(_lib.load().fa_decode_workspace_bytes(B, H, D, num_splits))
+
+
+def fa_decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, num_splits: int,
+                      scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                      want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Split-KV decode of one query token: q bf16 [B,H,1,D], k/v bf16 [B,H,Nk,D].
+    Returns (O bf16 [B,H,1,D], LSE fp32 [B,H] or None). ``workspace`` is a
+    device tensor of at least fa_decode_workspace_bytes(B,H,D,num_splits) bytes;
+    one is allocated when not given."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, torch.bfloat16)
+    B, H, one, D = q.shape
+    Nk = k.shape[2]
+    if one != 1:
+        raise ValueError("decode takes exactly one query token per (batch, head)")
+    if tuple(k.shape) != (B, H, Nk, D) or tuple(v.shape) != (B, H, Nk, D):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = fa_decode_workspace_bytes(B, H, D, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor("out", out, torch.bfloat16)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_tensor("lse", lse, torch.float32, ndim=2)
+    code = _lib.load().fa_decode_splitkv(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, workspace.data_ptr(), ws_bytes,
+        B, H, Nk, D, float(scale), int(num_splits), _stream(q))
+    _lib.check(code, "fa_decode_splitkv")
+    return out, lse

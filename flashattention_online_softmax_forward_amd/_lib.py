@@ -1,0 +1,58 @@
+"""ctypes loader for ``libfa_mi355x.so`` and the prototypes of include/fa.h."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+from .build import LIB_PATH
+
+FA_OK = 0
+STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_INVALID_ARG", 2: "FA_ERR_UNSUPPORTED", 3: "FA_ERR_LAUNCH"}
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+# name -> (restype, argtypes), in the order include/fa.h declares them.
+PROTOTYPES = {
+    "fa_forward": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp]),
+    "fa_forward_f32": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp]),
+    "fa_decode_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "fa_decode_splitkv": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _i, _i, _i, _i, _f, _i, _vp]),
+    "fa_status_string": (ctypes.c_char_p, [_i]),
+}
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library once. Raises if it has not been built: there is no
+    fallback implementation."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"HIP library not found at {path}; build it first "
+            "(python -m flashattention_online_softmax_forward_amd.build)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in PROTOTYPES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return load().fa_status_string(code).decode()
+
+
+class FAError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {status_string(code)}")
+
+
+def check(code: int, where: str) -> None:
+    if code != FA_OK:
+        raise FAError(code, where)

@@ -1,0 +1,119 @@
+// C ABI of the library (declared in include/fa.h): argument checks, then one
+// launch (two for decode) on the caller's stream. No allocation, no
+// synchronisation, no state.
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+bool good_scale(float s) { return std::isfinite(s) && s > 0.0f; }
+
+// Shared checks of the two forward entry points; `elem` is the element size.
+fa_status check_forward(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+                        int B, int H, int Nq, int Nk, int D, float scale, size_t elem, int bm,
+                        bool* nothing_to_do) {
+    *nothing_to_do = false;
+    if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return FA_ERR_INVALID_ARG;
+    if (!good_scale(scale)) return FA_ERR_INVALID_ARG;
+    if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * H * Nq == 0) {
+        *nothing_to_do = true;
+        return FA_OK;
+    }
+    if (Nk < 1) return FA_ERR_INVALID_ARG;
+    if (!Q || !K || !V || !O) return FA_ERR_INVALID_ARG;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return FA_ERR_INVALID_ARG;
+    if (LSE && !aligned4(LSE)) return FA_ERR_INVALID_ARG;
+    const long long nqb = ((long long)Nq + bm - 1) / bm;
+    if ((long long)B * H * nqb > INT_MAX) return FA_ERR_UNSUPPORTED;
+    const size_t bytes_q = (size_t)B * H * Nq * D * elem;
+    const size_t bytes_kv = (size_t)B * H * Nk * D * elem;
+    const size_t bytes_l = (size_t)B * H * Nq * sizeof(float);
+    if (overlaps(O, bytes_q, Q, bytes_q) || overlaps(O, bytes_q, K, bytes_kv) ||
+        overlaps(O, bytes_q, V, bytes_kv) || overlaps(O, bytes_q, LSE, bytes_l))
+        return FA_ERR_INVALID_ARG;
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status s) {
+    switch (s) {
+        case FA_OK: return "FA_OK";
+        case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument (pointer, size, alignment, scale or workspace)";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported head dimension or problem size";
+        case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: kernel launch failed";
+    }
+    return "FA_ERR_UNKNOWN: unknown status code";
+}
+
+fa_status fa_forward(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                     int B, int H, int Nq, int Nk, int D, float scale, int causal, hipStream_t stream) {
+    bool nothing = false;
+    const fa_status st = check_forward(Q, K, V, O, LSE, B, H, Nq, Nk, D, scale, 2, fa::BM_FWD, &nothing);
+    if (st != FA_OK || nothing) return st;
+    const fa::FwdArgs a{Q, K, V, O, LSE, B, H, Nq, Nk, D, scale, causal != 0, stream};
+    return fa::launch_fwd_bf16(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+fa_status fa_forward_f32(const float* Q, const float* K, const float* V, float* O, float* LSE,
+                         int B, int H, int Nq, int Nk, int D, float scale, int causal, hipStream_t stream) {
+    bool nothing = false;
+    const fa_status st = check_forward(Q, K, V, O, LSE, B, H, Nq, Nk, D, scale, 4, fa::BM_FWD_F32, &nothing);
+    if (st != FA_OK || nothing) return st;
+    const fa::FwdArgs a{Q, K, V, O, LSE, B, H, Nq, Nk, D, scale, causal != 0, stream};
+    return fa::launch_fwd_f32(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+size_t fa_decode_workspace_bytes(int B, int H, int D, int num_splits) {
+    if (B < 0 || H < 0 || num_splits < 1 || (D != 64 && D != 128)) return 0;
+    return (size_t)B * H * num_splits * (D + 2) * sizeof(float);
+}
+
+fa_status fa_decode_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                            void* workspace, size_t workspace_bytes, int B, int H, int Nk, int D,
+                            float scale, int num_splits, hipStream_t stream) {
+    if (B < 0 || H < 0 || Nk < 0 || num_splits < 1) return FA_ERR_INVALID_ARG;
+    if (!good_scale(scale)) return FA_ERR_INVALID_ARG;
+    if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * H == 0) return FA_OK;
+    if (Nk < 1) return FA_ERR_INVALID_ARG;
+    if (!Q || !K || !V || !O || !workspace) return FA_ERR_INVALID_ARG;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(workspace))
+        return FA_ERR_INVALID_ARG;
+    if (LSE && !aligned4(LSE)) return FA_ERR_INVALID_ARG;
+    if ((long long)B * H * num_splits > INT_MAX) return FA_ERR_UNSUPPORTED;
+    const size_t need = fa_decode_workspace_bytes(B, H, D, num_splits);
+    if (workspace_bytes < need) return FA_ERR_INVALID_ARG;
+    const size_t bytes_q = (size_t)B * H * D * 2;
+    const size_t bytes_kv = (size_t)B * H * Nk * D * 2;
+    if (overlaps(O, bytes_q, Q, bytes_q) || overlaps(O, bytes_q, K, bytes_kv) ||
+        overlaps(O, bytes_q, V, bytes_kv) || overlaps(O, bytes_q, LSE, (size_t)B * H * 4) ||
+        overlaps(workspace, need, Q, bytes_q) || overlaps(workspace, need, K, bytes_kv) ||
+        overlaps(workspace, need, V, bytes_kv) || overlaps(workspace, need, O, bytes_q) ||
+        overlaps(workspace, need, LSE, (size_t)B * H * 4))
+        return FA_ERR_INVALID_ARG;
+    const int chunk = (int)(((long long)Nk + num_splits - 1) / num_splits);
+    float* ws_o = static_cast<float*>(workspace);
+    float* ws_ml = ws_o + (size_t)B * H * num_splits * D;
+    const fa::DecodeArgs a{Q, K, V, O, LSE, ws_o, ws_ml, B, H, Nk, D, num_splits, chunk, scale, stream};
+    return fa::launch_decode(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // extern "C"

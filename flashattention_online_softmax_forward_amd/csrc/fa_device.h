@@ -1,0 +1,85 @@
+// Device-side helpers shared by the gfx950 attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Two fp32 values to a packed pair of bf16 (round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Low / high bf16 of a packed word widened to fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Hardware base-2 exponential (v_exp_f32); exp2(-inf) = 0.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Combine a value with the one held by lane (lane ^ 32): v_permlane32_swap
+// returns both halves, so a symmetric op of the two results is the same in
+// every lane.
+__device__ __forceinline__ float max_xor32(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// DPP lane moves inside a row of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+// Sum over aligned groups of N lanes (N = 4, 8 or 16); every lane of the
+// group ends with the group total.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(N == 4 || N == 8 || N == 16, "group of 4, 8 or 16 lanes");
+    x += dpp_mov<kDppQuadXor1>(x);
+    x += dpp_mov<kDppQuadXor2>(x);
+    if (N >= 8) x += dpp_mov<kDppRowHalfMirror>(x);
+    if (N >= 16) x += dpp_mov<kDppRowMirror>(x);
+    return x;
+}
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+    static_assert(N == 4 || N == 8 || N == 16, "group of 4, 8 or 16 lanes");
+    x = fmaxf(x, dpp_mov<kDppQuadXor1>(x));
+    x = fmaxf(x, dpp_mov<kDppQuadXor2>(x));
+    if (N >= 8) x = fmaxf(x, dpp_mov<kDppRowHalfMirror>(x));
+    if (N >= 16) x = fmaxf(x, dpp_mov<kDppRowMirror>(x));
+    return x;
+}
+
+// Workgroups are handed to the 8 XCDs round-robin (id % 8). Renumber them so
+// that each XCD runs a contiguous range of logical tiles: consecutive logical
+// tiles share K/V of one (batch, head), which then stays in that XCD's L2.
+__device__ __forceinline__ int xcd_logical_block(int id, int total) {
+    const int per = total / 8;
+    const int full = per * 8;
+    return id < full ? (id % 8) * per + id / 8 : id;
+}
+
+}  // namespace fa

@@ -1,0 +1,41 @@
+// Host-side launch interface between the C ABI (fa_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+constexpr int BM_FWD = 128;      // query rows per workgroup, bf16 forward
+constexpr int BM_FWD_F32 = 64;   // query rows per workgroup, fp32 forward
+
+struct FwdArgs {
+    const void* Q;
+    const void* K;
+    const void* V;
+    void* O;
+    float* LSE;
+    int B, H, Nq, Nk, D;
+    float scale;
+    int causal;
+    hipStream_t stream;
+};
+
+struct DecodeArgs {
+    const void* Q;
+    const void* K;
+    const void* V;
+    void* O;
+    float* LSE;
+    float* ws_o;     // [B*H, S, D] partial unnormalised outputs
+    float* ws_ml;    // [B*H, S, 2] partial (m in base 2, l)
+    int B, H, Nk, D, S, chunk;
+    float scale;
+    hipStream_t stream;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a);
+hipError_t launch_fwd_f32(const FwdArgs& a);
+hipError_t launch_decode(const DecodeArgs& a);
+
+}  // namespace fa

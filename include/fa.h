@@ -1,0 +1,114 @@
+/*
+ * fa.h — C ABI of the MI355X (gfx950) FlashAttention forward library.
+ *
+ * The operation (the same for every entry point) is exact softmax attention
+ *     O[b,h,i,:] = sum_j softmax_j(scale * Q[b,h,i,:] . K[b,h,j,:]) * V[b,h,j,:]
+ * computed without materialising the score matrix: a tile of queries stays on
+ * chip while tiles of keys/values stream past it, and each query row carries a
+ * running maximum m, a running denominator l and an unnormalised accumulator
+ * O that is rescaled by exp(m_old - m_new) whenever the maximum grows; O is
+ * divided by l once at the end. Sources: "11. Fusion, recompute, and flash
+ * attention" (ML compiler from scratch), sections 11.2, 11.6 and 11.9; the
+ * iThome FlashAttention article, section on the three running states; "Kernel
+ * visualization: Flash Attention 2", sections "Set up pointers and shared
+ * memory" and "Write the data back to HBM".
+ *
+ * Conventions shared by every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *     never allocates, frees, synchronises or prints. Every call only enqueues
+ *     kernels on `stream` (0 = the null stream) and returns.
+ *   - Layout is contiguous row-major [B, H, N, D] (head dimension fastest);
+ *     LSE is contiguous [B, H, Nq] fp32. Pointers must be 16-byte aligned.
+ *   - bf16 means IEEE bfloat16 stored as 16-bit words; outputs are rounded to
+ *     nearest-even. Accumulation, m and l are fp32.
+ *   - LSE (may be NULL to skip it) is the natural-log log-sum-exp of the
+ *     scaled scores of the row, m + ln(l), the per-row value the FA2 write-back
+ *     step stores beside O for a backward pass.
+ *   - scale must be finite and > 0 (the pages use 1/sqrt(D)).
+ *   - D (head dimension) must be 64 or 128.
+ *   - O must not overlap Q, K, V or LSE; inputs are never written.
+ *   - Sizes: B, H, Nq >= 0 (a zero size is a no-op returning FA_OK); Nk >= 1.
+ *   - Errors are reported before anything is enqueued, except FA_ERR_LAUNCH,
+ *     which reports hipGetLastError() after the launch. Calls are stateless and
+ *     thread-safe.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad size, bad scale, workspace too small */
+    FA_ERR_UNSUPPORTED = 2,   /* D not in {64, 128}, or a problem too large for the launch grid */
+    FA_ERR_LAUNCH = 3         /* the HIP runtime rejected a kernel launch */
+} fa_status;
+
+/*
+ * Prefill / full forward pass, bf16 in and out.
+ *   Q: bf16 [B,H,Nq,D]; K, V: bf16 [B,H,Nk,D]; O: bf16 [B,H,Nq,D] (written);
+ *   LSE: fp32 [B,H,Nq] (written) or NULL.
+ *   causal != 0: query row i attends keys j <= i only (absolute indices counted
+ *   from the first key, the rule of the exercise "Causal mask" on the ML
+ *   compiler page and of phobos' causal_attention); keys past Nk are never
+ *   attended (the masked last block of phobos' attention).
+ * Score and PV products use bf16 MFMA with fp32 accumulation; P is rounded to
+ * bf16 before the PV product.
+ */
+fa_status fa_forward(const void* Q, const void* K, const void* V,
+                     void* O, float* LSE,
+                     int B, int H, int Nq, int Nk, int D,
+                     float scale, int causal, hipStream_t stream);
+
+/*
+ * The same operation in fp32 end to end (fp32 inputs, fp32 arithmetic, fp32
+ * O), as the FA2 kernel sketch on "Kernel visualization: Flash Attention 2"
+ * computes it. Arguments as fa_forward.
+ */
+fa_status fa_forward_f32(const float* Q, const float* K, const float* V,
+                         float* O, float* LSE,
+                         int B, int H, int Nq, int Nk, int D,
+                         float scale, int causal, hipStream_t stream);
+
+/*
+ * Bytes of device workspace fa_decode_splitkv needs: B*H*num_splits*(D+2)*4
+ * (one fp32 partial state (m, l, o[D]) per head and key chunk). Returns 0 for
+ * invalid arguments.
+ */
+size_t fa_decode_workspace_bytes(int B, int H, int D, int num_splits);
+
+/*
+ * Flash-decoding: one query token per (b, h) over a whole key/value cache,
+ * no mask ("Flash-decoding" exercise on the ML compiler page). The Nk keys are
+ * split into num_splits chunks of c = ceil(Nk / num_splits) keys (chunk s is
+ * [s*c, min(Nk, (s+1)*c)); trailing chunks may be empty). A first kernel
+ * reduces each chunk to a partial (m, l, o) in `workspace`; a second kernel on
+ * the same stream merges the partials of each (b, h) with the rule of section
+ * 11.6 and writes O and LSE.
+ *   Q: bf16 [B,H,1,D]; K, V: bf16 [B,H,Nk,D]; O: bf16 [B,H,1,D];
+ *   LSE: fp32 [B,H] or NULL;
+ *   workspace: caller-owned device memory of at least
+ *   fa_decode_workspace_bytes(B,H,D,num_splits) bytes (workspace_bytes says
+ *   how much was passed); its contents on entry are ignored and are left
+ *   undefined. Calls that overlap in time must not share a workspace.
+ *   num_splits >= 1.
+ */
+fa_status fa_decode_splitkv(const void* Q, const void* K, const void* V,
+                            void* O, float* LSE,
+                            void* workspace, size_t workspace_bytes,
+                            int B, int H, int Nk, int D,
+                            float scale, int num_splits, hipStream_t stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* fa_status_string(fa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

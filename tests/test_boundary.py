@@ -1,0 +1,133 @@
+"""The C-ABI library on the CPU: it loads, exports every function include/fa.h
+declares, and rejects bad arguments before anything is enqueued. No call here
+reaches a kernel launch."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from flashattention_online_softmax_forward_amd import _lib
+from flashattention_online_softmax_forward_amd.build import LIB_PATH, build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+INVALID, UNSUPPORTED = 1, 2
+FAKE = 0x10000          # 16-byte aligned address that is never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB_PATH):
+        build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_api():
+    assert declared_functions() == sorted(
+        ["fa_forward", "fa_forward_f32", "fa_decode_workspace_bytes", "fa_decode_splitkv", "fa_status_string"])
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, f"{name} not exported"
+        assert name in _lib.PROTOTYPES, f"{name} has no ctypes prototype"
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings(lib):
+    for code, name in _lib.STATUS_NAMES.items():
+        assert lib.fa_status_string(code).decode().startswith(name)
+    assert lib.fa_status_string(99).decode().startswith("FA_ERR_UNKNOWN")
+
+
+def fwd(lib, fn="fa_forward", Q=FAKE, K=FAKE + 0x100000, V=FAKE + 0x200000, O=FAKE + 0x300000, L=None,
+        B=1, H=1, Nq=16, Nk=16, D=128, scale=0.125, causal=0):
+    return getattr(lib, fn)(Q, K, V, O, L, B, H, Nq, Nk, D, scale, causal, None)
+
+
+@pytest.mark.parametrize("fn", ["fa_forward", "fa_forward_f32"])
+def test_forward_rejects_bad_arguments(lib, fn):
+    assert fwd(lib, fn, Q=None) == INVALID
+    assert fwd(lib, fn, O=None) == INVALID
+    assert fwd(lib, fn, K=FAKE + 8) == INVALID                       # misaligned
+    assert fwd(lib, fn, L=FAKE + 0x400002) == INVALID                # misaligned LSE
+    assert fwd(lib, fn, B=-1) == INVALID
+    assert fwd(lib, fn, Nk=0) == INVALID
+    assert fwd(lib, fn, Nk=-3) == INVALID
+    assert fwd(lib, fn, scale=0.0) == INVALID
+    assert fwd(lib, fn, scale=-0.5) == INVALID
+    assert fwd(lib, fn, scale=float("inf")) == INVALID
+    assert fwd(lib, fn, scale=float("nan")) == INVALID
+    assert fwd(lib, fn, D=96) == UNSUPPORTED
+    assert fwd(lib, fn, D=256) == UNSUPPORTED
+    assert fwd(lib, fn, O=FAKE) == INVALID                           # O aliases Q
+    assert fwd(lib, fn, O=FAKE + 0x100000 + 64) == INVALID           # O overlaps K
+    assert fwd(lib, fn, B=65536, H=65536, Nq=1024) == UNSUPPORTED    # grid too large
+
+
+@pytest.mark.parametrize("fn", ["fa_forward", "fa_forward_f32"])
+def test_forward_empty_problem_is_a_noop(lib, fn):
+    # nothing to compute: returns before any pointer is looked at or any launch
+    assert fwd(lib, fn, Q=None, K=None, V=None, O=None, B=0) == 0
+    assert fwd(lib, fn, Q=None, K=None, V=None, O=None, H=0) == 0
+    assert fwd(lib, fn, Q=None, K=None, V=None, O=None, Nq=0) == 0
+
+
+def test_decode_workspace_bytes(lib):
+    assert lib.fa_decode_workspace_bytes(16, 32, 128, 64) == 16 * 32 * 64 * 130 * 4
+    assert lib.fa_decode_workspace_bytes(2, 3, 64, 5) == 2 * 3 * 5 * 66 * 4
+    assert lib.fa_decode_workspace_bytes(1, 1, 96, 4) == 0
+    assert lib.fa_decode_workspace_bytes(1, 1, 128, 0) == 0
+    assert lib.fa_decode_workspace_bytes(-1, 1, 128, 4) == 0
+
+
+def dec(lib, Q=FAKE, K=FAKE + 0x100000, V=FAKE + 0x200000, O=FAKE + 0x300000, L=None, W=FAKE + 0x400000,
+        wbytes=None, B=2, H=2, Nk=100, D=128, scale=0.1, S=4):
+    if wbytes is None:
+        wbytes = B * H * S * (D + 2) * 4 if B >= 0 and H >= 0 and S > 0 else 0
+    return lib.fa_decode_splitkv(Q, K, V, O, L, W, wbytes, B, H, Nk, D, scale, S, None)
+
+
+def test_decode_rejects_bad_arguments(lib):
+    assert dec(lib, W=None) == INVALID
+    assert dec(lib, wbytes=2 * 2 * 4 * 130 * 4 - 4) == INVALID       # workspace one float short
+    assert dec(lib, S=0) == INVALID
+    assert dec(lib, Nk=0) == INVALID
+    assert dec(lib, scale=0.0) == INVALID
+    assert dec(lib, D=80) == UNSUPPORTED
+    assert dec(lib, W=FAKE + 0x400004) == INVALID                    # misaligned workspace
+    assert dec(lib, W=FAKE + 0x100000) == INVALID                    # workspace overlaps K
+    assert dec(lib, B=0, Q=None, K=None, V=None, O=None, W=None) == 0
+
+
+def test_python_binding_refuses_cpu_tensors(lib):
+    import torch
+
+    import flashattention_online_softmax_forward_amd as fa
+
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="ROCm GPU"):
+        fa.fa_forward(q, q, q)
+    with pytest.raises(ValueError, match="ROCm GPU"):
+        fa.fa_decode_splitkv(q[:, :, :1], q, q, num_splits=2)
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "flashattention_online_softmax_forward_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f"{f} mentions the oracle"

@@ -1,0 +1,242 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Tolerances (stated by the workload definition): bf16 O max-abs <= 2e-2 and
+mean-abs <= 2e-3; fp32 O max-abs <= 1e-5. LSE is not given a bound there; the
+one used here follows from the arithmetic: fp32 accumulation of bf16 products
+(exact) over D <= 128 terms and an fp32 row sum give an LSE error of order
+1e-5 at these sizes, so 1e-3 (bf16 inputs) and 1e-5 (fp32) leave margin
+without hiding a wrong row.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import attention as orc
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX, BF16_MEAN, BF16_LSE = 2e-2, 2e-3, 1e-3
+F32_MAX, F32_LSE = 1e-5, 1e-5
+
+
+@pytest.fixture(scope="module")
+def fa():
+    if not torch.cuda.is_available():
+        pytest.skip("no ROCm GPU")
+    import flashattention_online_softmax_forward_amd as m
+    from flashattention_online_softmax_forward_amd import _lib
+
+    _lib.load()
+    return m
+
+
+DEV = "cuda:0"
+
+
+def f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def report(tag, err_o, err_l):
+    print(f"[parity] {tag}: O max {err_o.max():.3e} mean {err_o.mean():.3e}  LSE max {err_l.max():.3e}", flush=True)
+
+
+def check_bf16(tag, o, lse, ro, rl):
+    err_o = np.abs(f64(o) - ro) if isinstance(o, torch.Tensor) else np.abs(o - ro)
+    err_l = np.abs((f64(lse) if isinstance(lse, torch.Tensor) else lse) - rl)
+    report(tag, err_o, err_l)
+    assert np.isfinite(err_o).all() and np.isfinite(err_l).all(), tag
+    assert err_o.max() <= BF16_MAX, tag
+    assert err_o.mean() <= BF16_MEAN, tag
+    assert err_l.max() <= BF16_LSE, tag
+
+
+# ---------------------------------------------------------------- fp32 path
+
+F32_CASES = [
+    # (B, H, Nq, Nk, D, causal)
+    (1, 1, 256, 256, 64, False),      # the single-head fp32 workload
+    (1, 1, 256, 256, 64, True),
+    (2, 2, 200, 200, 128, False),
+    (1, 3, 131, 131, 128, True),
+    (1, 1, 77, 300, 64, False),
+    (1, 1, 77, 300, 64, True),
+    (1, 1, 1, 1, 64, False),
+]
+
+
+@pytest.mark.parametrize("case", F32_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_fp32_matches_oracle(fa, case):
+    B, H, Nq, Nk, D, causal = case
+    q, k, v = synth.make_qkv(B, H, Nq, Nk, D, torch.float32, seed=11)
+    print(f"[case] fp32 {case}", flush=True)
+    o, lse = fa.fa_forward_f32(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal)
+    torch.cuda.synchronize()
+    ro, rl = orc.attention(f64(q), f64(k), f64(v), 1.0 / math.sqrt(D), causal)
+    err_o, err_l = np.abs(f64(o) - ro), np.abs(f64(lse) - rl)
+    report(f"fp32 {case}", err_o, err_l)
+    assert err_o.max() <= F32_MAX and err_l.max() <= F32_LSE
+
+
+# ---------------------------------------------------------------- bf16, small sizes, every row
+
+BF16_CASES = [
+    # (B, H, Nq, Nk, D, causal, qk_mul)
+    (1, 2, 256, 256, 128, False, 1.0),
+    (1, 2, 256, 256, 128, True, 1.0),
+    (1, 2, 256, 256, 64, False, 1.0),
+    (1, 2, 256, 256, 64, True, 1.0),
+    (2, 3, 300, 300, 64, True, 1.0),       # ragged: 300 = 2*128 + 44
+    (1, 2, 300, 300, 128, False, 1.0),
+    (1, 1, 1, 1, 128, False, 1.0),
+    (1, 1, 1, 1, 64, True, 1.0),
+    (1, 1, 17, 17, 128, True, 1.0),
+    (1, 1, 77, 300, 128, False, 1.0),      # Nq < Nk
+    (1, 1, 77, 300, 128, True, 1.0),       # top-left causal with Nq < Nk
+    (1, 1, 300, 77, 64, True, 1.0),        # Nq > Nk: late rows see every key
+    (1, 4, 513, 513, 128, True, 3.0),      # rescale stress (scores std ~ 9)
+    (1, 2, 1000, 1000, 64, True, 1.0),
+    (2, 2, 129, 1025, 128, False, 3.0),
+]
+
+
+@pytest.mark.parametrize("case", BF16_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_bf16_matches_oracle(fa, case):
+    B, H, Nq, Nk, D, causal, mul = case
+    q, k, v = synth.make_qkv(B, H, Nq, Nk, D, torch.bfloat16, seed=12, qk_mul=mul)
+    print(f"[case] bf16 {case}", flush=True)
+    o, lse = fa.fa_forward(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal)
+    torch.cuda.synchronize()
+    ro, rl = orc.attention(f64(q), f64(k), f64(v), 1.0 / math.sqrt(D), causal)
+    check_bf16(f"bf16 {case}", o, lse, ro, rl)
+
+
+def test_bf16_late_max_in_last_tile(fa):
+    """A row whose largest score sits in its last key tile (the case the
+    'forgot to rescale o' bug fails): keys grow with their index."""
+    D, N = 128, 640
+    q = torch.ones(1, 1, N, D, dtype=torch.bfloat16)
+    ramp = torch.linspace(-2.0, 2.0, N).view(1, 1, N, 1)
+    k = (ramp * torch.ones(1, 1, N, D)).to(torch.bfloat16)
+    v = synth.normal((1, 1, N, D), torch.bfloat16, 13, synth.V_ID)
+    for causal in (False, True):
+        o, lse = fa.fa_forward(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal)
+        torch.cuda.synchronize()
+        ro, rl = orc.attention(f64(q), f64(k), f64(v), 1.0 / math.sqrt(D), causal)
+        check_bf16(f"late max causal={causal}", o, lse, ro, rl)
+
+
+# ---------------------------------------------------------------- closed forms and invariants on the GPU
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_zero_keys_give_prefix_means(fa, D):
+    """K = 0: causal row i is the mean of V[0..i] and LSE = ln(i+1); non-causal
+    rows are the column mean with LSE = ln(Nk). Independent of the oracle."""
+    N = 333
+    q = synth.normal((1, 2, N, D), torch.bfloat16, 14, synth.Q_ID)
+    k = torch.zeros(1, 2, N, D, dtype=torch.bfloat16)
+    v = synth.normal((1, 2, N, D), torch.bfloat16, 14, synth.V_ID)
+    vd = f64(v)
+    o, lse = fa.fa_forward(q.to(DEV), k.to(DEV), v.to(DEV), causal=True)
+    torch.cuda.synchronize()
+    prefix = np.cumsum(vd, axis=2) / np.arange(1, N + 1)[None, None, :, None]
+    check_bf16(f"K=0 causal D={D}", o, lse, prefix, np.broadcast_to(np.log(np.arange(1, N + 1)), (1, 2, N)))
+    o, lse = fa.fa_forward(q.to(DEV), k.to(DEV), v.to(DEV), causal=False)
+    torch.cuda.synchronize()
+    check_bf16(f"K=0 full D={D}", o, lse, np.broadcast_to(vd.mean(axis=2, keepdims=True), vd.shape),
+               np.full((1, 2, N), math.log(N)))
+
+
+def test_ones_values_and_causal_first_row(fa):
+    B, H, N, D = 1, 3, 400, 128
+    q, k, v = synth.make_qkv(B, H, N, N, D, torch.bfloat16, seed=15, qk_mul=3.0)
+    ones = torch.ones_like(v)
+    for causal in (False, True):
+        o, _ = fa.fa_forward(q.to(DEV), k.to(DEV), ones.to(DEV), causal=causal)
+        torch.cuda.synchronize()
+        assert np.abs(f64(o) - 1.0).max() <= 2.0 ** -8, "V = 1 must give O = 1"
+    o, _ = fa.fa_forward(q.to(DEV), k.to(DEV), v.to(DEV), causal=True)
+    torch.cuda.synchronize()
+    # row 0 attends key 0 only: O = V[0] up to one bf16 rounding
+    assert np.abs(f64(o)[:, :, 0] - f64(v)[:, :, 0]).max() <= 2.0 ** -8 * np.abs(f64(v)[:, :, 0]).max()
+    ofull, _ = fa.fa_forward(q.to(DEV), k.to(DEV), v.to(DEV), causal=False)
+    torch.cuda.synchronize()
+    # the last row sees every key: causal and full agree bit for bit
+    assert torch.equal(o[:, :, -1].cpu(), ofull[:, :, -1].cpu())
+
+
+def test_permuting_keys_and_values(fa):
+    B, H, N, D = 1, 2, 320, 128
+    q, k, v = synth.make_qkv(B, H, N, N, D, torch.bfloat16, seed=16)
+    perm = torch.randperm(N, generator=torch.Generator().manual_seed(17))
+    o1, l1 = fa.fa_forward(q.to(DEV), k.to(DEV), v.to(DEV))
+    o2, l2 = fa.fa_forward(q.to(DEV), k[:, :, perm].contiguous().to(DEV), v[:, :, perm].contiguous().to(DEV))
+    torch.cuda.synchronize()
+    assert np.abs(f64(o1) - f64(o2)).max() <= 2e-2
+    assert np.abs(f64(l1) - f64(l2)).max() <= 1e-3
+
+
+def test_run_to_run_bitwise(fa):
+    """No atomics and a fixed reduction order: two runs agree bit for bit
+    (a missing LDS barrier would show up here as a difference)."""
+    for (B, H, N, D, causal) in [(1, 8, 1100, 128, True), (1, 8, 1100, 64, False)]:
+        q, k, v = synth.make_qkv(B, H, N, N, D, torch.bfloat16, seed=18, device=DEV)
+        a = fa.fa_forward(q, k, v, causal=causal)
+        b = fa.fa_forward(q, k, v, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    q, k, v = synth.make_qkv(4, 8, 1, 5000, 128, torch.bfloat16, seed=19, device=DEV)
+    a = fa.fa_decode_splitkv(q, k, v, num_splits=16)
+    b = fa.fa_decode_splitkv(q, k, v, num_splits=16)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_lse_optional(fa):
+    q, k, v = synth.make_qkv(1, 2, 200, 200, 128, torch.bfloat16, seed=20, device=DEV)
+    o1, _ = fa.fa_forward(q, k, v, causal=True)
+    o2, l2 = fa.fa_forward(q, k, v, causal=True, want_lse=False)
+    torch.cuda.synchronize()
+    assert l2 is None and torch.equal(o1, o2)
+
+
+# ---------------------------------------------------------------- split-KV decode
+
+DECODE_CASES = [
+    # (B, H, Nk, D, num_splits)
+    (2, 3, 1000, 128, 1),
+    (2, 3, 1000, 128, 2),
+    (2, 3, 1000, 128, 7),
+    (2, 3, 1000, 64, 64),
+    (1, 2, 37, 128, 64),       # more splits than keys: empty chunks
+    (1, 2, 37, 64, 37),
+    (1, 1, 1, 128, 3),
+    (3, 5, 4097, 128, 16),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_decode_matches_oracle(fa, case):
+    B, H, Nk, D, S = case
+    q, k, v = synth.make_qkv(B, H, 1, Nk, D, torch.bfloat16, seed=21)
+    print(f"[case] decode {case}", flush=True)
+    o, lse = fa.fa_decode_splitkv(q.to(DEV), k.to(DEV), v.to(DEV), num_splits=S)
+    torch.cuda.synchronize()
+    ro, rl = orc.decode(f64(q), f64(k), f64(v), 1.0 / math.sqrt(D))
+    check_bf16(f"decode {case}", o, lse, ro, rl[:, :, 0])
+
+
+def test_decode_agrees_with_forward(fa):
+    q, k, v = synth.make_qkv(2, 4, 1, 3000, 128, torch.bfloat16, seed=22, device=DEV)
+    of, lf = fa.fa_forward(q, k, v)
+    for S in (1, 2, 64, 3000):
+        od, ld = fa.fa_decode_splitkv(q, k, v, num_splits=S)
+        torch.cuda.synchronize()
+        assert np.abs(f64(od) - f64(of)).max() <= 2e-2
+        assert np.abs(f64(ld) - f64(lf)[:, :, 0]).max() <= 1e-3

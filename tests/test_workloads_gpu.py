@@ -1,0 +1,102 @@
+"""GPU parity at the full workload sizes, in the launch configuration the bench
+times (the same library call on the same seeded device-resident inputs).
+The oracle checks a sample of rows of every (batch, head) — the first 64, the
+last 64 (which hold any ragged tail) and 64 seeded random rows — and, for the
+decode workload, 64 of its (batch, head) pairs; each sampled row is computed
+by the oracle in full against all keys of its head."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import attention as orc
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+BF16_MAX, BF16_MEAN, BF16_LSE = 2e-2, 2e-3, 1e-3
+
+
+@pytest.fixture(scope="module")
+def fa():
+    if not torch.cuda.is_available():
+        pytest.skip("no ROCm GPU")
+    import flashattention_online_softmax_forward_amd as m
+
+    return m
+
+
+def f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def sample_rows(n, seed):
+    rng = np.random.default_rng(seed)
+    rows = set(range(min(64, n))) | set(range(max(0, n - 64), n)) | set(rng.integers(0, n, 64).tolist())
+    return np.array(sorted(rows))
+
+
+def check_prefill(fa, w, seed=0):
+    q, k, v = synth.make_workload(w, seed=seed, device=DEV)
+    print(f"[case] {w.name}", flush=True)
+    if w.dtype == torch.float32:
+        o, lse = fa.fa_forward_f32(q, k, v, causal=w.causal, scale=w.scale)
+    else:
+        o, lse = fa.fa_forward(q, k, v, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.Nq, seed + 1)
+    rows_t = torch.as_tensor(rows, device=DEV)
+    worst_o, worst_l, sum_o, count = 0.0, 0.0, 0.0, 0
+    for b in range(w.B):
+        for h in range(w.H):
+            ro, rl = orc.attention_rows(f64(q[b, h].index_select(0, rows_t)), rows, f64(k[b, h]), f64(v[b, h]),
+                                        w.scale, w.causal)
+            eo = np.abs(f64(o[b, h].index_select(0, rows_t)) - ro)
+            el = np.abs(f64(lse[b, h].index_select(0, rows_t)) - rl)
+            assert np.isfinite(eo).all() and np.isfinite(el).all()
+            worst_o, worst_l = max(worst_o, eo.max()), max(worst_l, el.max())
+            sum_o += eo.sum()
+            count += eo.size
+    mean_o = sum_o / count
+    print(f"[parity] {w.name}: O max {worst_o:.3e} mean {mean_o:.3e} LSE max {worst_l:.3e}", flush=True)
+    if w.dtype == torch.float32:
+        assert worst_o <= 1e-5 and worst_l <= 1e-5
+    else:
+        assert worst_o <= BF16_MAX and mean_o <= BF16_MEAN and worst_l <= BF16_LSE
+
+
+@pytest.mark.parametrize("name", [n for n, w in synth.WORKLOADS.items() if not w.is_decode])
+def test_prefill_workload(fa, name):
+    check_prefill(fa, synth.WORKLOADS[name])
+
+
+def test_ragged_16001(fa):
+    """16000 is a multiple of 128; one more row makes every tile size ragged."""
+    w = synth.WORKLOADS["causal_b1_h16_n16000_d64"]
+    check_prefill(fa, synth.Workload("causal_b1_h16_n16001_d64", 1, 16, 16001, 16001, 64, torch.bfloat16, causal=True))
+    assert w.Nq == 16000
+
+
+def test_decode_workload(fa):
+    w = synth.WORKLOADS["decode_b16_h32_kv32768_d128_s64"]
+    q, k, v = synth.make_workload(w, seed=0, device=DEV)
+    print(f"[case] {w.name}", flush=True)
+    o, lse = fa.fa_decode_splitkv(q, k, v, num_splits=w.num_splits, scale=w.scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    pairs = {(0, 0), (w.B - 1, w.H - 1)} | {(int(b), int(h)) for b, h in zip(rng.integers(0, w.B, 62), rng.integers(0, w.H, 62))}
+    worst_o, worst_l, sum_o, count = 0.0, 0.0, 0.0, 0
+    for b, h in sorted(pairs):
+        ro, rl = orc.attention_rows(f64(q[b, h]), [0], f64(k[b, h]), f64(v[b, h]), w.scale, False)
+        eo = np.abs(f64(o[b, h]) - ro)
+        el = abs(float(lse[b, h]) - rl[0])
+        worst_o, worst_l = max(worst_o, eo.max()), max(worst_l, el)
+        sum_o += eo.sum()
+        count += eo.size
+    mean_o = sum_o / count
+    print(f"[parity] {w.name}: {len(pairs)} heads, O max {worst_o:.3e} mean {mean_o:.3e} LSE max {worst_l:.3e}",
+          flush=True)
+    assert worst_o <= BF16_MAX and mean_o <= BF16_MEAN and worst_l <= BF16_LSE
