@@ -19,14 +19,26 @@
 //     in-lane reductions plus one exchange with lane ^ 32.
 //   * The rows of K fed to the A operand are permuted (bits 2 and 3 of the row
 //     index swapped) so the accumulator registers of S^T, rounded to bf16, are
-//     already the B operand of the second MFMA, O^T += V^T P^T, whose A operand
-//     reads 8 consecutive keys of one V column from a transposed LDS copy of V.
-//     P never leaves registers.
+//     already the B operand of the second MFMA, O^T += V^T P^T. P never leaves
+//     registers.
 //   * O^T lives in 16*D/32 fp32 accumulators per lane, one query row per lane,
 //     so the alpha rescale is a per-lane scalar multiply.
-//   * K/V tiles are loaded with coalesced 16-byte global loads into registers
-//     one tile ahead, then written to LDS (K row-major with a 16-byte pad, V
-//     transposed with an XOR swizzle of its 16-byte chunks).
+//   * K and V tiles go from global memory straight into LDS
+//     (global_load_lds_dwordx4: no VGPR staging), two tiles deep, one barrier
+//     per tile. Both are row-major in LDS with an XOR swizzle of their 16-byte
+//     chunks chosen so the MFMA operand reads are free of bank conflicts. The
+//     V^T operand (8 consecutive keys of one column per lane) is read with
+//     ds_read_b64_tr_b16, the LDS transpose read: within each 16-lane block,
+//     source lane s points at 4 consecutive columns of key k0 + s/4, and lane
+//     i receives column i of those 4 keys. Rows past Nk are clamped to the
+//     last key instead of branching: they are masked out of S, and their
+//     (finite) values are multiplied by P = 0.
+//   * Conditional rescaling (the FA4 refinement the iThome article describes
+//     after the alpha derivation): the running maximum of a wave's rows is
+//     only moved, and O and l rescaled, when some row's tile maximum exceeds it
+//     by more than 2^8 (base 2). Otherwise the tile is exponentiated against
+//     the stale maximum (P <= 256, safe in fp32 and bf16), which is exact once
+//     O is divided by the l accumulated on the same base.
 //   * Causal: key tiles past the block's last row are never visited, tiles a
 //     whole wave cannot see are skipped by that wave, masks are applied only on
 //     diagonal and ragged tiles, and the heaviest query blocks are issued first.
@@ -42,6 +54,8 @@ template <> struct Bf16Tile<64> { static constexpr int BN = 128; };
 
 constexpr int kFwdWaves = 4;
 constexpr int kFwdThreads = 64 * kFwdWaves;
+// Growth of a row maximum (log2 units) that forces a rescale of O and l.
+constexpr float kRescaleThreshold = 8.0f;
 
 // Key row (within a 32-key block) that lane-row i of the S^T A operand reads:
 // bits 2 and 3 swapped. With it, accumulator register r of lane (j, h) holds
@@ -50,10 +64,21 @@ __device__ __forceinline__ int s_row_perm(int i) {
     return (i & ~0xC) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
 
-// Physical 16-byte chunk of logical chunk c in row d of the transposed V tile.
-__device__ __forceinline__ int vt_chunk(int d, int c) {
-    return c ^ ((d ^ (d >> 3)) & 7);
+// 16-byte chunk swizzles (CPR = chunks per row; LDS banks span 256 bytes).
+// K: the 16 rows read together by one MFMA operand hit 16 distinct bank groups.
+template <int CPR>
+__device__ __forceinline__ int k_swz(int row) {
+    return CPR == 16 ? (row & 15) : ((row >> 1) & 7);
 }
+// V: the 4 keys x 4 column-quads of a transpose-read block, and the two blocks
+// that share a key range, hit distinct bank groups.
+template <int CPR>
+__device__ __forceinline__ int v_swz(int key) {
+    return CPR == 16 ? 4 * (key & 3) : 4 * ((key >> 1) & 1);
+}
+
+#define LDS_AS __attribute__((address_space(3)))
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kFwdThreads, 2)
@@ -61,20 +86,22 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
                      const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
                      float* __restrict__ LSEg, int Nq, int Nk, int nqb, float scale2) {
     constexpr int BN = Bf16Tile<D>::BN;
-    constexpr int KP = D + 8;                  // K tile row pitch (elements)
+    constexpr int TILE = BN * D;               // elements of one K (or V) tile
     constexpr int NCB = BN / 32;               // 32-key blocks of S^T
     constexpr int NKK = D / 16;                // 16-wide d steps of the S MFMA
     constexpr int NDB = D / 32;                // 32-wide d blocks of O^T
     constexpr int NPV = BN / 16;               // 16-key steps of the PV MFMA
     constexpr int CPR = D / 8;                 // 16-byte chunks per row
-    constexpr int NKL = BN * CPR / kFwdThreads;
-    constexpr int DG = D / 8;                  // V loader: 8-wide d groups
-    constexpr int KG = kFwdThreads / DG;       // V loader: groups of 4 keys
-    static_assert(KG * 4 == BN, "V loader covers the tile");
-    static_assert(NKL * kFwdThreads == BN * CPR, "K loader covers the tile");
+    constexpr int NLD = BN * CPR / kFwdThreads;   // DMA chunks per thread per tensor
+    static_assert(NLD * kFwdThreads == BN * CPR, "loader covers the tile");
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * KP];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * BN];
+    // Two K/V tile buffers. Four distinct arrays, selected statically (the
+    // loop below is unrolled by two), let the compiler see that a DMA into one
+    // buffer never aliases reads of the other, so it adds no wait between them.
+    __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[TILE];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -108,47 +135,29 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     if (CAUSAL) kend = min(Nk, min(q0 + BM_FWD, Nq));
     const int ntiles = (kend + BN - 1) / BN;
 
-    u32x4_t kreg[NKL];
-    u32x4_t vreg[4];
-    const int vdg = tid % DG;
-    const int vkg = tid / DG;
+    // Per-thread DMA slots: chunk p = (i*4 + wave)*64 + lane of the tile lands
+    // at byte 16*p of the LDS tile, and holds logical chunk (p % CPR) ^ swz(row).
+    int ld_row[NLD], ld_kcol[NLD], ld_vcol[NLD];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+        const int p = (i * kFwdWaves + wave) * 64 + lane;
+        ld_row[i] = p / CPR;
+        ld_kcol[i] = ((p % CPR) ^ k_swz<CPR>(ld_row[i])) * 8;
+        ld_vcol[i] = ((p % CPR) ^ v_swz<CPR>(ld_row[i])) * 8;
+    }
 
-    auto load_tile = [&](int kv0) {
+    auto issue_tile = [&](int kv0, uint16_t* kb, uint16_t* vb) {
+        const int last = Nk - 1 - kv0;
+        const uint16_t* Kt = K + (size_t)kv0 * D;
+        const uint16_t* Vt_g = V + (size_t)kv0 * D;
 #pragma unroll
-        for (int i = 0; i < NKL; ++i) {
-            const int c = tid + i * kFwdThreads;
-            const int row = c / CPR, col = c % CPR;
-            const int key = kv0 + row;
-            kreg[i] = key < Nk ? *(const u32x4_t*)(K + (size_t)key * D + col * 8) : u32x4_t{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int key = kv0 + vkg * 4 + r;
-            vreg[r] = key < Nk ? *(const u32x4_t*)(V + (size_t)key * D + vdg * 8) : u32x4_t{0u, 0u, 0u, 0u};
-        }
-    };
-
-    auto store_tile = [&]() {
-#pragma unroll
-        for (int i = 0; i < NKL; ++i) {
-            const int c = tid + i * kFwdThreads;
-            const int row = c / CPR, col = c % CPR;
-            *(u32x4_t*)(Ks + row * KP + col * 8) = kreg[i];
-        }
-        // 4 keys x 8 d held as 4 rows of 8 -> 8 rows (one per d) of 4 keys.
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            uint32_t w0, w1;
-            if ((e & 1) == 0) {
-                w0 = (vreg[0][e >> 1] & 0xffffu) | (vreg[1][e >> 1] << 16);
-                w1 = (vreg[2][e >> 1] & 0xffffu) | (vreg[3][e >> 1] << 16);
-            } else {
-                w0 = (vreg[0][e >> 1] >> 16) | (vreg[1][e >> 1] & 0xffff0000u);
-                w1 = (vreg[2][e >> 1] >> 16) | (vreg[3][e >> 1] & 0xffff0000u);
-            }
-            const int d = vdg * 8 + e;
-            const int chunk = vt_chunk(d, vkg >> 1);
-            *(u32x2_t*)(Vt + d * BN + chunk * 8 + (vkg & 1) * 4) = u32x2_t{w0, w1};
+        for (int i = 0; i < NLD; ++i) {
+            const int row = min(ld_row[i], last);
+            const int slot = (i * kFwdWaves + wave) * 64 * 8;      // elements
+            __builtin_amdgcn_global_load_lds((const void*)(Kt + (uint32_t)(row * D + ld_kcol[i])),
+                                             (LDS_AS void*)(LDS_AS uint16_t*)(kb + slot), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(Vt_g + (uint32_t)(row * D + ld_vcol[i])),
+                                             (LDS_AS void*)(LDS_AS uint16_t*)(vb + slot), 16, 0, 0);
         }
     };
 
@@ -158,95 +167,129 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc_o[db][r] = 0.f;
 
-    float m_run = -INFINITY;   // running max of the base-2 scaled scores
+    float m_run = -INFINITY;   // base-2 scaled maximum the row is accumulated against
     float l_run = 0.f;         // this lane's half of the running sum
 
+    // K operand address (element offset within a K tile) for block c, step kk.
     const int srow = s_row_perm(j);
+    // V transpose-read addresses: lane s of 16-lane block b points at key
+    // 16*tt + 8*h + 4*rd + s/4, columns 32*db + 16*(b%2) + 4*(s%4) .. +3.
+    const int vb_blk = (lane >> 4) & 1;
+    const int v_s = lane & 15;
 
-    if (ntiles > 0) load_tile(0);
-    for (int t = 0; t < ntiles; ++t) {
+    // One key tile: prefetch tile t+1 into the other buffer, compute tile t.
+    auto step = [&](int t, const uint16_t* kb, const uint16_t* vb, uint16_t* kb_next, uint16_t* vb_next) {
         const int kv0 = t * BN;
-        __syncthreads();
-        store_tile();
-        __syncthreads();
-        if (t + 1 < ntiles) load_tile(kv0 + BN);
+        if (t + 1 < ntiles) issue_tile(kv0 + BN, kb_next, vb_next);
 
-        if (CAUSAL && kv0 > wrow0 + 31) continue;   // no row of this wave sees the tile
-
-        // S^T = K Q^T for NCB blocks of 32 keys.
-        f32x16_t s[NCB];
+        // A wave skips a causal tile that lies entirely after all its rows.
+        if (!CAUSAL || kv0 <= wrow0 + 31) {
+            // S^T = K Q^T for NCB blocks of 32 keys.
+            f32x16_t s[NCB];
 #pragma unroll
-        for (int c = 0; c < NCB; ++c) {
+            for (int c = 0; c < NCB; ++c) {
+                const int row = c * 32 + srow;
+                const int sw = k_swz<CPR>(row);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[c][r] = 0.f;
+                for (int r = 0; r < 16; ++r) s[c][r] = 0.f;
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                const bf16x8_t a = *(const bf16x8_t*)(Ks + (c * 32 + srow) * KP + kk * 16 + h * 8);
-                s[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[c], 0, 0, 0);
+                for (int kk = 0; kk < NKK; ++kk) {
+                    const bf16x8_t a = *(const bf16x8_t*)(kb + row * D + (((kk * 2 + h) ^ sw) * 8));
+                    s[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[c], 0, 0, 0);
+                }
             }
-        }
 
-        // Mask keys past Nk and, on diagonal tiles, keys after the row.
-        const bool ragged = kv0 + BN > Nk;
-        const bool diag = CAUSAL && (kv0 + BN - 1 > wrow0);
-        if (ragged || diag) {
+            // Mask keys past Nk and, on diagonal tiles, keys after the row.
+            const bool ragged = kv0 + BN > Nk;
+            const bool diag = CAUSAL && (kv0 + BN - 1 > wrow0);
+            if (ragged || diag) {
+#pragma unroll
+                for (int c = 0; c < NCB; ++c)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = kv0 + c * 32 + (r >> 3) * 16 + h * 8 + (r & 7);
+                        const bool dead = key >= Nk || (CAUSAL && key > qrow);
+                        if (dead) s[c][r] = -INFINITY;
+                    }
+            }
+
+            // Tile row max (raw scores; scale2 > 0) in base-2 units.
+            float mx = s[0][0];
 #pragma unroll
             for (int c = 0; c < NCB; ++c)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kv0 + c * 32 + (r >> 3) * 16 + h * 8 + (r & 7);
-                    const bool dead = key >= Nk || (CAUSAL && key > qrow);
-                    if (dead) s[c][r] = -INFINITY;
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[c][r]);
+            const float m_tile = max_xor32(mx) * scale2;
+
+            // Move the maximum (and rescale O, l) only when some row of the
+            // wave outgrew it by more than the threshold.
+            if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleThreshold)) {
+                const float m_new = fmaxf(m_run, m_tile);
+                const float alpha = exp2_hw(m_run - m_new);
+                m_run = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
+            }
+
+            // P = exp2(S*scale2 - m), row sum of this half, bf16 B operands.
+            bf16x8_t pf[NPV];
+            float lsum = 0.f;
+#pragma unroll
+            for (int c = 0; c < NCB; ++c)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    float p[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        p[e] = exp2_hw(__builtin_fmaf(s[c][u * 8 + e], scale2, -m_run));
+                        lsum += p[e];
+                    }
+                    u32x4_t w;
+                    w[0] = pack_bf16x2(p[0], p[1]);
+                    w[1] = pack_bf16x2(p[2], p[3]);
+                    w[2] = pack_bf16x2(p[4], p[5]);
+                    w[3] = pack_bf16x2(p[6], p[7]);
+                    pf[c * 2 + u] = __builtin_bit_cast(bf16x8_t, w);
+                }
+            l_run += lsum;
+
+            // O^T += V^T P^T: A operand = 8 keys (16*tt + 8*h ..) of column
+            // 32*db + j, gathered by two transpose reads of 4 keys each.
+#pragma unroll
+            for (int tt = 0; tt < NPV; ++tt)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    bf16x4_t part[2];
+#pragma unroll
+                    for (int rd = 0; rd < 2; ++rd) {
+                        const int key = tt * 16 + h * 8 + rd * 4 + (v_s >> 2);
+                        const int col = db * 32 + vb_blk * 16 + (v_s & 3) * 4;
+                        const int chunk = (col >> 3) ^ v_swz<CPR>(key);
+                        const uint16_t* addr = vb + key * D + chunk * 8 + (col & 7);
+                        part[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                            (LDS_AS bf16x4_t*)(LDS_AS uint16_t*)addr);
+                    }
+                    const bf16x8_t a = {part[0][0], part[0][1], part[0][2], part[0][3],
+                                        part[1][0], part[1][1], part[1][2], part[1][3]};
+                    acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[tt], acc_o[db], 0, 0, 0);
                 }
         }
 
-        // Row max (raw scores; scale2 > 0), then the new base-2 maximum.
-        float mx = s[0][0];
-#pragma unroll
-        for (int c = 0; c < NCB; ++c)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[c][r]);
-        mx = max_xor32(mx);
-        const float m_new = fmaxf(m_run, mx * scale2);
-        const float alpha = exp2_hw(m_run - m_new);
-        m_run = m_new;
+        if (t + 1 < ntiles) {
+            __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): tile t+1 landed (this wave's part)
+            __syncthreads();                    // ... every wave's part; all reads of tile t done
+        }
+    };
 
-        // P = exp2(S*scale2 - m_new), row sum of this half, bf16 B operands.
-        bf16x8_t pf[NPV];
-        float lsum = 0.f;
-#pragma unroll
-        for (int c = 0; c < NCB; ++c)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                float p[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    p[e] = exp2_hw(__builtin_fmaf(s[c][u * 8 + e], scale2, -m_new));
-                    lsum += p[e];
-                }
-                u32x4_t w;
-                w[0] = pack_bf16x2(p[0], p[1]);
-                w[1] = pack_bf16x2(p[2], p[3]);
-                w[2] = pack_bf16x2(p[4], p[5]);
-                w[3] = pack_bf16x2(p[6], p[7]);
-                pf[c * 2 + u] = __builtin_bit_cast(bf16x8_t, w);
-            }
-        l_run = l_run * alpha + lsum;
-
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
-
-        // O^T += V^T P^T: A = V^T rows d = 32*db + j, keys 16*tt + 8*h .. +7.
-#pragma unroll
-        for (int tt = 0; tt < NPV; ++tt)
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const int d = db * 32 + j;
-                const bf16x8_t a = *(const bf16x8_t*)(Vt + d * BN + vt_chunk(d, tt * 2 + h) * 8);
-                acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[tt], acc_o[db], 0, 0, 0);
-            }
+    issue_tile(0, k_lds0, v_lds0);
+    __builtin_amdgcn_s_waitcnt(0xF70);          // vmcnt(0): this wave's DMA landed
+    __syncthreads();
+    for (int t = 0; t < ntiles; t += 2) {
+        step(t, k_lds0, v_lds0, k_lds1, v_lds1);
+        if (t + 1 < ntiles) step(t + 1, k_lds1, v_lds1, k_lds0, v_lds0);
     }
 
     // Epilogue: O / l to bf16, LSE = (m + log2 l) * ln 2.
