@@ -52,7 +52,7 @@ template <int D> struct Bf16Tile;
 template <> struct Bf16Tile<128> { static constexpr int BN = 64; };
 template <> struct Bf16Tile<64> { static constexpr int BN = 128; };
 
-constexpr int kFwdWaves = 4;
+constexpr int kFwdWaves = 8;
 constexpr int kFwdThreads = 64 * kFwdWaves;
 // Growth of a row maximum (log2 units) that forces a rescale of O and l.
 constexpr float kRescaleThreshold = 8.0f;
@@ -80,11 +80,14 @@ __device__ __forceinline__ int v_swz(int key) {
 #define LDS_AS __attribute__((address_space(3)))
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kFwdThreads, 2)
+template <int D>
+__global__ __launch_bounds__(kFwdThreads, 1)
 void fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                      const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
-                     float* __restrict__ LSEg, int Nq, int Nk, int nqb, float scale2) {
+                     float* __restrict__ LSEg, int Nq, int Nk, int nqb, float scale2, int causal) {
+    // The causal flag is a uniform run-time argument rather than a template
+    // parameter: one code shape for both keeps register allocation stable.
+    const bool CAUSAL = causal != 0;
     constexpr int BN = Bf16Tile<D>::BN;
     constexpr int TILE = BN * D;               // elements of one K (or V) tile
     constexpr int NCB = BN / 32;               // 32-key blocks of S^T
@@ -92,19 +95,22 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     constexpr int NDB = D / 32;                // 32-wide d blocks of O^T
     constexpr int NPV = BN / 16;               // 16-key steps of the PV MFMA
     constexpr int CPR = D / 8;                 // 16-byte chunks per row
-    constexpr int NLD = BN * CPR / kFwdThreads;   // DMA chunks per thread per tensor
-    static_assert(NLD * kFwdThreads == BN * CPR, "loader covers the tile");
+    constexpr int kLoadWaves = kFwdWaves / 2;     // group 0 issues every tile load
+    constexpr int NLD = BN * CPR / (64 * kLoadWaves);   // DMA chunks per thread per tensor
+    static_assert(NLD * 64 * kLoadWaves == BN * CPR, "loader covers the tile");
 
-    // Two K/V tile buffers. Four distinct arrays, selected statically (the
-    // loop below is unrolled by two), let the compiler see that a DMA into one
-    // buffer never aliases reads of the other, so it adds no wait between them.
+    // Two K and two V tile buffers. Four distinct arrays, selected statically
+    // (the phase loop below is unrolled over two tiles), let the compiler see
+    // that a DMA into one buffer never aliases reads of another, so it adds no
+    // wait between them.
     __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[TILE];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
+    const int group = wave >> 2;               // ping-pong group (one wave of each per SIMD)
     const int lane = tid & 63;
     const int j = lane & 31;
     const int h = lane >> 5;
@@ -134,30 +140,30 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     int kend = Nk;
     if (CAUSAL) kend = min(Nk, min(q0 + BM_FWD, Nq));
     const int ntiles = (kend + BN - 1) / BN;
+    // Tiles this wave computes: a causal tile entirely after all its rows is skipped.
+    const int my_tiles = CAUSAL ? min(ntiles, (wrow0 + 31) / BN + 1) : ntiles;
 
-    // Per-thread DMA slots: chunk p = (i*4 + wave)*64 + lane of the tile lands
-    // at byte 16*p of the LDS tile, and holds logical chunk (p % CPR) ^ swz(row).
+    // DMA slots (group 0 only): chunk p = (i*4 + wave)*64 + lane of a tile
+    // lands at byte 16*p of the LDS tile and holds logical chunk
+    // (p % CPR) ^ swz(row).
+    const int lwave = wave & (kLoadWaves - 1);
     int ld_row[NLD], ld_kcol[NLD], ld_vcol[NLD];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-        const int p = (i * kFwdWaves + wave) * 64 + lane;
+        const int p = (i * kLoadWaves + lwave) * 64 + lane;
         ld_row[i] = p / CPR;
         ld_kcol[i] = ((p % CPR) ^ k_swz<CPR>(ld_row[i])) * 8;
         ld_vcol[i] = ((p % CPR) ^ v_swz<CPR>(ld_row[i])) * 8;
     }
-
-    auto issue_tile = [&](int kv0, uint16_t* kb, uint16_t* vb) {
+    auto dma = [&](const uint16_t* src, const int* col, int kv0, uint16_t* dst) __attribute__((always_inline)) {
         const int last = Nk - 1 - kv0;
-        const uint16_t* Kt = K + (size_t)kv0 * D;
-        const uint16_t* Vt_g = V + (size_t)kv0 * D;
+        const uint16_t* base = src + (size_t)kv0 * D;
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
             const int row = min(ld_row[i], last);
-            const int slot = (i * kFwdWaves + wave) * 64 * 8;      // elements
-            __builtin_amdgcn_global_load_lds((const void*)(Kt + (uint32_t)(row * D + ld_kcol[i])),
-                                             (LDS_AS void*)(LDS_AS uint16_t*)(kb + slot), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void*)(Vt_g + (uint32_t)(row * D + ld_vcol[i])),
-                                             (LDS_AS void*)(LDS_AS uint16_t*)(vb + slot), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(base + (uint32_t)(row * D + col[i])),
+                                             (LDS_AS void*)(LDS_AS uint16_t*)(dst + (i * kLoadWaves + lwave) * 512),
+                                             16, 0, 0);
         }
     };
 
@@ -166,131 +172,196 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc_o[db][r] = 0.f;
+    f32x16_t s[NCB];            // S^T of the tile between its MFMA step and its softmax step
+    bf16x8_t pf[NPV];           // P of the tile between its softmax step and its PV step
 
     float m_run = -INFINITY;   // base-2 scaled maximum the row is accumulated against
     float l_run = 0.f;         // this lane's half of the running sum
 
-    // K operand address (element offset within a K tile) for block c, step kk.
     const int srow = s_row_perm(j);
-    // V transpose-read addresses: lane s of 16-lane block b points at key
-    // 16*tt + 8*h + 4*rd + s/4, columns 32*db + 16*(b%2) + 4*(s%4) .. +3.
     const int vb_blk = (lane >> 4) & 1;
     const int v_s = lane & 15;
 
-    // One key tile: prefetch tile t+1 into the other buffer, compute tile t.
-    auto step = [&](int t, const uint16_t* kb, const uint16_t* vb, uint16_t* kb_next, uint16_t* vb_next) {
-        const int kv0 = t * BN;
-        if (t + 1 < ntiles) issue_tile(kv0 + BN, kb_next, vb_next);
-
-        // A wave skips a causal tile that lies entirely after all its rows.
-        if (!CAUSAL || kv0 <= wrow0 + 31) {
-            // S^T = K Q^T for NCB blocks of 32 keys.
-            f32x16_t s[NCB];
+    // MFMA step of tile t: O^T += V^T P^T for tile t-1, then S^T = K Q^T for tile t.
+    // Only one wave per SIMD is in this step at a time, so it must keep the
+    // matrix core busy on its own: LDS operands are read a few MFMAs ahead, and
+    // sched_group_barrier pins that order (DS reads first, then one MFMA per
+    // group of reads).
+    constexpr int NPVM = NPV * NDB;            // PV MFMAs per tile
+    constexpr int NSM = NKK * NCB;             // QK MFMAs per tile
+    constexpr int LEAD = 4;                    // MFMAs of operand prefetch
+    auto pv_operand = [&](const uint16_t* vb_prev, int i) __attribute__((always_inline)) {
+        const int tt = i / NDB, db = i % NDB;
+        bf16x4_t part[2];
 #pragma unroll
-            for (int c = 0; c < NCB; ++c) {
-                const int row = c * 32 + srow;
-                const int sw = k_swz<CPR>(row);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[c][r] = 0.f;
-#pragma unroll
-                for (int kk = 0; kk < NKK; ++kk) {
-                    const bf16x8_t a = *(const bf16x8_t*)(kb + row * D + (((kk * 2 + h) ^ sw) * 8));
-                    s[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[c], 0, 0, 0);
-                }
-            }
-
-            // Mask keys past Nk and, on diagonal tiles, keys after the row.
-            const bool ragged = kv0 + BN > Nk;
-            const bool diag = CAUSAL && (kv0 + BN - 1 > wrow0);
-            if (ragged || diag) {
-#pragma unroll
-                for (int c = 0; c < NCB; ++c)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = kv0 + c * 32 + (r >> 3) * 16 + h * 8 + (r & 7);
-                        const bool dead = key >= Nk || (CAUSAL && key > qrow);
-                        if (dead) s[c][r] = -INFINITY;
-                    }
-            }
-
-            // Tile row max (raw scores; scale2 > 0) in base-2 units.
-            float mx = s[0][0];
-#pragma unroll
-            for (int c = 0; c < NCB; ++c)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[c][r]);
-            const float m_tile = max_xor32(mx) * scale2;
-
-            // Move the maximum (and rescale O, l) only when some row of the
-            // wave outgrew it by more than the threshold.
-            if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleThreshold)) {
-                const float m_new = fmaxf(m_run, m_tile);
-                const float alpha = exp2_hw(m_run - m_new);
-                m_run = m_new;
-                l_run *= alpha;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
-            }
-
-            // P = exp2(S*scale2 - m), row sum of this half, bf16 B operands.
-            bf16x8_t pf[NPV];
-            float lsum = 0.f;
-#pragma unroll
-            for (int c = 0; c < NCB; ++c)
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    float p[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        p[e] = exp2_hw(__builtin_fmaf(s[c][u * 8 + e], scale2, -m_run));
-                        lsum += p[e];
-                    }
-                    u32x4_t w;
-                    w[0] = pack_bf16x2(p[0], p[1]);
-                    w[1] = pack_bf16x2(p[2], p[3]);
-                    w[2] = pack_bf16x2(p[4], p[5]);
-                    w[3] = pack_bf16x2(p[6], p[7]);
-                    pf[c * 2 + u] = __builtin_bit_cast(bf16x8_t, w);
-                }
-            l_run += lsum;
-
-            // O^T += V^T P^T: A operand = 8 keys (16*tt + 8*h ..) of column
-            // 32*db + j, gathered by two transpose reads of 4 keys each.
-#pragma unroll
-            for (int tt = 0; tt < NPV; ++tt)
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    bf16x4_t part[2];
-#pragma unroll
-                    for (int rd = 0; rd < 2; ++rd) {
-                        const int key = tt * 16 + h * 8 + rd * 4 + (v_s >> 2);
-                        const int col = db * 32 + vb_blk * 16 + (v_s & 3) * 4;
-                        const int chunk = (col >> 3) ^ v_swz<CPR>(key);
-                        const uint16_t* addr = vb + key * D + chunk * 8 + (col & 7);
-                        part[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                            (LDS_AS bf16x4_t*)(LDS_AS uint16_t*)addr);
-                    }
-                    const bf16x8_t a = {part[0][0], part[0][1], part[0][2], part[0][3],
-                                        part[1][0], part[1][1], part[1][2], part[1][3]};
-                    acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[tt], acc_o[db], 0, 0, 0);
-                }
+        for (int rd = 0; rd < 2; ++rd) {
+            const int key = tt * 16 + h * 8 + rd * 4 + (v_s >> 2);
+            const int col = db * 32 + vb_blk * 16 + (v_s & 3) * 4;
+            const int chunk = (col >> 3) ^ v_swz<CPR>(key);
+            const uint16_t* addr = vb_prev + key * D + chunk * 8 + (col & 7);
+            part[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t*)(LDS_AS uint16_t*)addr);
         }
-
-        if (t + 1 < ntiles) {
-            __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): tile t+1 landed (this wave's part)
-            __syncthreads();                    // ... every wave's part; all reads of tile t done
+        return bf16x8_t{part[0][0], part[0][1], part[0][2], part[0][3],
+                        part[1][0], part[1][1], part[1][2], part[1][3]};
+    };
+    auto qk_operand = [&](const uint16_t* kb, int i) __attribute__((always_inline)) {
+        const int kk = i / NCB, c = i % NCB;
+        const int row = c * 32 + srow;
+        return *(const bf16x8_t*)(kb + row * D + (((kk * 2 + h) ^ k_swz<CPR>(row)) * 8));
+    };
+    auto step_mfma = [&](int t, const uint16_t* kb, const uint16_t* vb_prev) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_setprio(1);
+        const bool do_pv = t >= 1 && t - 1 < my_tiles;
+        const bool do_qk = t < my_tiles;
+        if (do_pv && do_qk) {
+            // PV(t-1) then QK(t) as one stream of 2*16 MFMAs, each operand read
+            // LEAD MFMAs ahead of its use.
+            constexpr int NM = NPVM + NSM;
+            auto operand = [&](int i) __attribute__((always_inline)) {
+                return i < NPVM ? pv_operand(vb_prev, i) : qk_operand(kb, i - NPVM);
+            };
+            const f32x16_t zero = {};
+            bf16x8_t ring[LEAD];
+#pragma unroll
+            for (int i = 0; i < LEAD; ++i) ring[i] = operand(i);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * LEAD, 0);
+#pragma unroll
+            for (int i = 0; i < NM; ++i) {
+                const bf16x8_t a = ring[i % LEAD];
+                if (i + LEAD < NM) ring[i % LEAD] = operand(i + LEAD);
+                if (i < NPVM)
+                    acc_o[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[i / NDB], acc_o[i % NDB], 0, 0, 0);
+                else  // the first d step of each key block starts from zero
+                    s[(i - NPVM) % NCB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        a, qf[(i - NPVM) / NCB], (i - NPVM) < NCB ? zero : s[(i - NPVM) % NCB], 0, 0, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                const int nx = i + LEAD;
+                if (nx < NPVM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                else if (nx < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        } else if (do_pv) {
+#pragma unroll
+            for (int i = 0; i < NPVM; ++i)
+                acc_o[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv_operand(vb_prev, i), pf[i / NDB],
+                                                                         acc_o[i % NDB], 0, 0, 0);
+        } else if (do_qk) {
+            const f32x16_t zero = {};
+#pragma unroll
+            for (int i = 0; i < NSM; ++i)
+                s[i % NCB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qk_operand(kb, i), qf[i / NCB],
+                                                                     i < NCB ? zero : s[i % NCB], 0, 0, 0);
         }
+        __builtin_amdgcn_s_setprio(0);
     };
 
-    issue_tile(0, k_lds0, v_lds0);
-    __builtin_amdgcn_s_waitcnt(0xF70);          // vmcnt(0): this wave's DMA landed
+    // Softmax step of tile t: mask, row max, conditional rescale, P and its row sum.
+    auto step_softmax = [&](int t) __attribute__((always_inline)) {
+        if (t < 0 || t >= my_tiles) return;
+        const int kv0 = t * BN;
+        const bool ragged = kv0 + BN > Nk;
+        const bool diag = CAUSAL && (kv0 + BN - 1 > wrow0);
+        if (ragged || diag) {
+#pragma unroll
+            for (int c = 0; c < NCB; ++c)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kv0 + c * 32 + (r >> 3) * 16 + h * 8 + (r & 7);
+                    const bool dead = key >= Nk || (CAUSAL && key > qrow);
+                    if (dead) s[c][r] = -INFINITY;
+                }
+        }
+        float mx = s[0][0];
+#pragma unroll
+        for (int c = 0; c < NCB; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[c][r]);
+        const float m_tile = max_xor32(mx) * scale2;
+        // Move the maximum (and rescale O, l) only when some row of the wave
+        // outgrew it by more than the threshold.
+        if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleThreshold)) {
+            const float m_new = fmaxf(m_run, m_tile);
+            const float alpha = exp2_hw(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
+        }
+        float lsum = 0.f;
+#pragma unroll
+        for (int c = 0; c < NCB; ++c)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                float p[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    p[e] = exp2_hw(__builtin_fmaf(s[c][u * 8 + e], scale2, -m_run));
+                    lsum += p[e];
+                }
+                u32x4_t w;
+                w[0] = pack_bf16x2(p[0], p[1]);
+                w[1] = pack_bf16x2(p[2], p[3]);
+                w[2] = pack_bf16x2(p[4], p[5]);
+                w[3] = pack_bf16x2(p[6], p[7]);
+                pf[c * 2 + u] = __builtin_bit_cast(bf16x8_t, w);
+            }
+        l_run += lsum;
+    };
+
+    // Ping-pong schedule. Every wave runs the same sequence of steps
+    //     M(0) | S(0) | M(1) | S(1) | ... | M(T)
+    // separated by workgroup barriers, where M(t) = PV(t-1) + QK(t) on the
+    // matrix core and S(t) = softmax of tile t on the VALU. Group 1 executes
+    // one extra barrier first (and group 0 one at the end): barriers match by
+    // count, so group 1 always runs one step behind group 0 and, on every SIMD,
+    // one wave feeds the matrix core while the other does softmax.
+    // Tile buffers: K(t) in k_lds[t%2], V(t) in v_lds[t%2]. Group 0 issues the
+    // DMA of K(t+1) and V(t) at the start of its M(t) and waits for it at the
+    // end of its S(t): the next barrier publishes it, one step before group 0
+    // and two before group 1 first read it, and after the last read (group 1's
+    // M(t-1)) of the buffers it overwrites.
+    // Wave-uniform by construction; readfirstlane makes that visible, so the
+    // conditional barriers below are scalar branches.
+    const bool loader = __builtin_amdgcn_readfirstlane(group) == 0;
+    // One M step and one S step. The barrier between them protects no LDS data
+    // (it only keeps the two groups a step apart), so it is a plain s_barrier
+    // without the memory fence of __syncthreads, which would otherwise wait
+    // for the tile DMA still in flight. The barrier after the S step publishes
+    // the DMA that the loader waves have just waited for.
+    auto tile_steps = [&](int t, const uint16_t* kb, const uint16_t* vb_prev, uint16_t* kb_next,
+                          uint16_t* vb_cur) __attribute__((always_inline)) {
+        step_mfma(t, kb, vb_prev);
+        if (loader && t < ntiles) {
+            if (t + 1 < ntiles) dma(K, ld_kcol, (t + 1) * BN, kb_next);
+            dma(V, ld_vcol, t * BN, vb_cur);
+        }
+        // sched_barrier(0): no instruction moves across the step boundary, so
+        // the two steps keep their own (smaller) sets of live registers.
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        step_softmax(t);
+        // vmcnt(0) on every wave (a no-op for waves with no DMA in flight), so
+        // the compiler knows no tile DMA is pending past this point.
+        __builtin_amdgcn_s_waitcnt(0xF70);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    if (loader) dma(K, ld_kcol, 0, k_lds0);
+    __builtin_amdgcn_s_waitcnt(0xF70);
     __syncthreads();
-    for (int t = 0; t < ntiles; t += 2) {
-        step(t, k_lds0, v_lds0, k_lds1, v_lds1);
-        if (t + 1 < ntiles) step(t + 1, k_lds1, v_lds1, k_lds0, v_lds0);
+    if (!loader) __builtin_amdgcn_s_barrier();
+    // Steps M(t), S(t) for t = 0 .. ntiles (M(ntiles) is the last PV product,
+    // S(ntiles) is empty); two tiles per iteration keep buffer choice static.
+    for (int t = 0; t <= ntiles; t += 2) {
+        tile_steps(t, k_lds0, v_lds1, k_lds1, v_lds0);
+        if (t + 1 > ntiles) break;
+        tile_steps(t + 1, k_lds1, v_lds0, k_lds0, v_lds1);
     }
+    if (loader) __builtin_amdgcn_s_barrier();
 
     // Epilogue: O / l to bf16, LSE = (m + log2 l) * ln 2.
     const float l_tot = sum_xor32(l_run);
@@ -311,19 +382,18 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D>
 static hipError_t launch_one(const FwdArgs& a) {
     const int nqb = (a.Nq + BM_FWD - 1) / BM_FWD;
     const int grid = a.B * a.H * nqb;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(grid), dim3(kFwdThreads), 0, a.stream,
+    hipLaunchKernelGGL((fwd_bf16_kernel<D>), dim3(grid), dim3(kFwdThreads), 0, a.stream,
                        (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
-                       (uint16_t*)a.O, a.LSE, a.Nq, a.Nk, nqb, a.scale * kLog2e);
+                       (uint16_t*)a.O, a.LSE, a.Nq, a.Nk, nqb, a.scale * kLog2e, a.causal);
     return hipGetLastError();
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
-    if (a.D == 128) return a.causal ? launch_one<128, true>(a) : launch_one<128, false>(a);
-    return a.causal ? launch_one<64, true>(a) : launch_one<64, false>(a);
+    return a.D == 128 ? launch_one<128>(a) : launch_one<64>(a);
 }
 
 }  // namespace fa

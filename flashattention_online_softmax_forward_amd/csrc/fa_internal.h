@@ -6,7 +6,7 @@
 
 namespace fa {
 
-constexpr int BM_FWD = 128;      // query rows per workgroup, bf16 forward
+constexpr int BM_FWD = 256;      // query rows per workgroup, bf16 forward (8 waves x 32)
 constexpr int BM_FWD_F32 = 64;   // query rows per workgroup, fp32 forward
 
 struct FwdArgs {
