@@ -6,9 +6,11 @@ resident in HBM. The metric's second half, split-KV decode bandwidth, is
 measured in the same run on the decode workload (B=16, H=32, one query,
 Nk=32768, D=128, 64 splits) and reported under "decode". Prints ONE JSON line.
 
-Timing: W untimed warm-up steps, then K steps between two HIP events recorded
-on the stream the kernels are launched on (torch's current stream, which is
-the stream handed to the library), synchronised on both sides.
+Timing: W untimed warm-up steps plus untimed steps until half a second of GPU
+work has run (the engine clock ramps up under load), then K steps between two
+HIP events recorded on the stream the kernels are launched on (torch's current
+stream, which is the stream handed to the library), synchronised on both
+sides.
 
 Algorithmic counts (not the implementation's):
   prefill FLOPs = 4*B*H*Nq*Nk*D (halved when causal)
@@ -66,9 +68,18 @@ def workload_counts(w):
     return flops, bytes_
 
 
-def time_steps(fn, steps, warmup, torch):
+def time_steps(fn, steps, warmup, torch, settle_s=0.5):
+    """W warm-up calls, then keep calling (untimed) until ``settle_s`` seconds
+    of GPU work have run, so the engine clock has ramped up before the timed
+    region; then K timed calls between two events on the launch stream."""
     for _ in range(warmup):
         fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < settle_s:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -115,11 +126,11 @@ def cpu_baseline(w, q, k, v, budget_s):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="prefill_b1_h32_n2048_d128")
     ap.add_argument("--decode-workload", default="decode_b16_h32_kv32768_d128_s64")
-    ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")

@@ -270,12 +270,18 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
                     if (dead) s[c][r] = -INFINITY;
                 }
         }
-        float mx = s[0][0];
+        // Row max and row sum as several independent chains (a single chain
+        // of dependent max / add instructions would leave the VALU waiting on
+        // its own latency).
+        constexpr int NCH = 4;
+        float mxc[NCH];
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) mxc[k] = s[0][k];
 #pragma unroll
         for (int c = 0; c < NCB; ++c)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[c][r]);
-        const float m_tile = max_xor32(mx) * scale2;
+            for (int r = 0; r < 16; ++r) mxc[r % NCH] = fmaxf(mxc[r % NCH], s[c][r]);
+        const float m_tile = max_xor32(fmaxf(fmaxf(mxc[0], mxc[1]), fmaxf(mxc[2], mxc[3]))) * scale2;
         // Move the maximum (and rescale O, l) only when some row of the wave
         // outgrew it by more than the threshold.
         if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleThreshold)) {
@@ -288,7 +294,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
         }
-        float lsum = 0.f;
+        float lsc[NCH] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < NCB; ++c)
 #pragma unroll
@@ -297,7 +303,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     p[e] = exp2_hw(__builtin_fmaf(s[c][u * 8 + e], scale2, -m_run));
-                    lsum += p[e];
+                    lsc[e % NCH] += p[e];
                 }
                 u32x4_t w;
                 w[0] = pack_bf16x2(p[0], p[1]);
@@ -306,6 +312,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
                 w[3] = pack_bf16x2(p[6], p[7]);
                 pf[c * 2 + u] = __builtin_bit_cast(bf16x8_t, w);
             }
+        const float lsum = (lsc[0] + lsc[1]) + (lsc[2] + lsc[3]);
         l_run += lsum;
     };
 
