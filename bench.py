@@ -102,24 +102,31 @@ def cpu_baseline(w, q, k, v, budget_s):
 
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     flops_head = 4.0 * w.Nq * w.Nk * w.D * (0.5 if w.causal else 1.0)
-    done, t_total = 0, 0.0
-    for (b, h) in heads:
-        qh = q[b, h].float().cpu().numpy().astype(np.float64)[None, None]
-        kh = k[b, h].float().cpu().numpy().astype(np.float64)[None, None]
-        vh = v[b, h].float().cpu().numpy().astype(np.float64)[None, None]
-        t0 = time.perf_counter()
-        orc.attention(qh, kh, vh, w.scale, w.causal)
-        t_total += time.perf_counter() - t0
-        done += 1
-        if t_total >= budget_s:
-            break
+    done, t_total, passes = 0, 0.0, 0
+    widened = {}
+    # Whole heads in order, over and over (the workload is one pass) until the
+    # budget is spent; only the oracle call itself is timed.
+    while t_total < budget_s:
+        for (b, h) in heads:
+            if (b, h) not in widened:
+                widened[(b, h)] = tuple(x[b, h].float().cpu().numpy().astype(np.float64)[None, None]
+                                        for x in (q, k, v))
+            qh, kh, vh = widened[(b, h)]
+            t0 = time.perf_counter()
+            orc.attention(qh, kh, vh, w.scale, w.causal)
+            t_total += time.perf_counter() - t0
+            done += 1
+            if t_total >= budget_s:
+                break
+        passes += 1
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {
         "value": flops_head * done / t_total / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{done} of {len(heads)} heads of {w.name} (fp64 two-pass, every row), {t_total:.1f} s",
+        "sample": f"{done} head computations ({done / len(heads):.2f} passes over the {len(heads)} heads) of "
+                  f"{w.name}, fp64 two-pass, every row, {t_total:.1f} s",
     }
 
 
@@ -133,7 +140,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of attention, time a plain device copy of this many bytes "
                          "(calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
