@@ -4,15 +4,16 @@
 // Kernel 1 (partial): one workgroup per (head, key chunk). The chunk's keys are
 // streamed once from HBM with fully coalesced 16-byte loads: D/8 lanes share a
 // key row (each lane owns 8 of the D columns), so one wave instruction reads
-// 1 KiB of consecutive rows. Each lane group keeps its own online-softmax state
+// 1 KiB of consecutive rows. The loads are non-temporal: every byte of the
+// cache is read exactly once, so it should not displace anything in L2/MALL. Each lane group keeps its own online-softmax state
 // (m, l, o) over the keys it visits, updated a block of U keys at a time
 // (iThome article, "three states"); at the end the group states are merged in
 // LDS with the merge rule of section 11.6 and the chunk's partial (m, l, o) is
 // written to the workspace. This work is bandwidth-bound (one FMA per byte), so
 // it stays on the vector ALUs: there is no contraction worth an MFMA here.
 //
-// Kernel 2 (combine): one workgroup of D threads per (batch, head) merges the
-// chunk partials with the same rule, M = max m_s, l = sum l_s 2^(m_s - M),
+// Kernel 2 (combine): one workgroup per (batch, head) merges the chunk
+// partials with the same rule, M = max m_s, l = sum l_s 2^(m_s - M),
 // o = sum o_s 2^(m_s - M), and writes O = o / l (bf16) and
 // LSE = (M + log2 l) ln 2. Empty chunks carry (-inf, 0, 0) and weigh nothing.
 
@@ -71,8 +72,8 @@ void decode_partial_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __re
         for (int u = 0; u < U; ++u) {
             const int key = base + u * G;
             if (key < j1) {
-                kr[u] = *(const u32x4_t*)(K + (size_t)key * D);
-                vr[u] = *(const u32x4_t*)(V + (size_t)key * D);
+                kr[u] = __builtin_nontemporal_load((const u32x4_t*)(K + (size_t)key * D));
+                vr[u] = __builtin_nontemporal_load((const u32x4_t*)(V + (size_t)key * D));
             } else {
                 kr[u] = u32x4_t{0u, 0u, 0u, 0u};
                 vr[u] = u32x4_t{0u, 0u, 0u, 0u};
@@ -147,26 +148,68 @@ void decode_partial_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __re
     }
 }
 
+constexpr int kCombThreads = 256;
+
+// Combine: 256 threads per (batch, head); thread = (split group sg, column
+// quad dq). Each thread folds splits sg, sg + SG, ... of its 4 columns (float4
+// loads, several in flight), then the SG partial states are merged in LDS.
 template <int D>
-__global__ __launch_bounds__(D)
+__global__ __launch_bounds__(kCombThreads)
 void decode_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
                            uint16_t* __restrict__ Og, float* __restrict__ LSEg, int S) {
+    constexpr int DQ = D / 4;                       // column quads
+    constexpr int SG = kCombThreads / DQ;           // split groups
+    __shared__ float sm_max[kCombThreads];
+    __shared__ float sm_l[SG];
+    __shared__ __attribute__((aligned(16))) float sm_o[SG * D];
+
     const int bh = blockIdx.x;
-    const int d = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int dq = tid % DQ;
+    const int sg = tid / DQ;
     const float* ml = ws_ml + (size_t)bh * S * 2;
-    const float* po = ws_o + (size_t)bh * S * D + d;
+    const float* po = ws_o + (size_t)bh * S * D + dq * 4;
+
+    // Global maximum over all splits (every thread scans a strided share).
     float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
-    float L = 0.f, acc = 0.f;
-    for (int s = 0; s < S; ++s) {
+    for (int s = tid; s < S; s += kCombThreads) M = fmaxf(M, ml[2 * s]);
+    sm_max[tid] = M;
+    __syncthreads();
+    for (int w = kCombThreads / 2; w > 0; w >>= 1) {
+        if (tid < w) sm_max[tid] = fmaxf(sm_max[tid], sm_max[tid + w]);
+        __syncthreads();
+    }
+    M = sm_max[0];
+
+    // This thread's splits: l and o rescaled to M and summed (empty chunks,
+    // m = -inf, weigh nothing).
+    float L = 0.f;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int s = sg; s < S; s += SG) {
         const float ms = ml[2 * s];
         const float w = ms == -INFINITY ? 0.f : exp2_hw(ms - M);
         L = __builtin_fmaf(w, ml[2 * s + 1], L);
-        acc = __builtin_fmaf(w, po[(size_t)s * D], acc);
+        const f32x4_t o = *(const f32x4_t*)(po + (size_t)s * D);
+        acc[0] = __builtin_fmaf(w, o[0], acc[0]);
+        acc[1] = __builtin_fmaf(w, o[1], acc[1]);
+        acc[2] = __builtin_fmaf(w, o[2], acc[2]);
+        acc[3] = __builtin_fmaf(w, o[3], acc[3]);
     }
-    const float out = acc / L;
-    Og[(size_t)bh * D + d] = __builtin_bit_cast(uint16_t, (__bf16)out);
-    if (d == 0 && LSEg) LSEg[bh] = (M + __log2f(L)) * kLn2;
+    *(f32x4_t*)(sm_o + sg * D + dq * 4) = acc;
+    if (dq == 0) sm_l[sg] = L;
+    __syncthreads();
+
+    if (tid < D) {
+        float lt = 0.f, ot = 0.f;
+#pragma unroll
+        for (int g = 0; g < SG; ++g) {
+            lt += sm_l[g];
+            ot += sm_o[g * D + tid];
+        }
+        Og[(size_t)bh * D + tid] = __builtin_bit_cast(uint16_t, (__bf16)(ot / lt));
+        if (tid == 0 && LSEg) LSEg[bh] = (M + __log2f(lt)) * kLn2;
+    }
 }
 
 template <int D>
@@ -177,8 +220,8 @@ static hipError_t launch_d(const DecodeArgs& a) {
                        a.Nk, a.S, a.chunk, a.scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(BH), dim3(D), 0, a.stream, a.ws_o, a.ws_ml,
-                       (uint16_t*)a.O, a.LSE, a.S);
+    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(BH), dim3(kCombThreads), 0, a.stream, a.ws_o,
+                       a.ws_ml, (uint16_t*)a.O, a.LSE, a.S);
     return hipGetLastError();
 }
 
