@@ -132,6 +132,50 @@ def test_bf16_late_max_in_last_tile(fa):
         check_bf16(f"late max causal={causal}", o, lse, ro, rl)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_rescale_threshold_paths(fa, D, causal):
+    """Row maxima that grow, tile after tile, by amounts just under, just over
+    and far over the 2^8 rescale threshold (base 2), then stop growing. Every
+    query row's scores are q . k_j = a_j with a single non-zero coordinate, so
+    the per-key base-2 score is a_j * scale * log2(e) exactly as designed."""
+    N = 1024
+    scale = 1.0 / math.sqrt(D)
+    c2 = scale / math.log(2.0)                    # base-2 score per unit of a_j
+    rng = np.random.default_rng(30)
+    steps = [0.0, 7.9, 15.8, 23.9, 44.0, 104.0, 104.5, 110.0]   # tile maxima (log2 units)
+    a = np.empty(N)
+    tile = 64
+    for t0 in range(0, N, tile):
+        top = steps[min(t0 // tile, len(steps) - 1)]
+        a[t0:t0 + tile] = (top - rng.uniform(0.0, 12.0, tile)) / c2
+        a[t0 + int(rng.integers(0, tile))] = top / c2
+    q = torch.zeros(1, 2, N, D)
+    q[..., 0] = 1.0
+    k = torch.zeros(1, 2, N, D)
+    k[..., 0] = torch.from_numpy(a).float()
+    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    v = synth.normal((1, 2, N, D), torch.bfloat16, 31, synth.V_ID)
+    o, lse = fa.fa_forward(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal)
+    torch.cuda.synchronize()
+    ro, rl = orc.attention(f64(q), f64(k), f64(v), scale, causal)
+    check_bf16(f"rescale paths D={D} causal={causal}", o, lse, ro, rl)
+
+
+def test_huge_score_magnitudes(fa):
+    """Q and K of magnitude ~20: scores of order 10^3..10^4, the softmax is
+    one-hot and the stale-maximum path must never overflow."""
+    q, k, v = synth.make_qkv(1, 2, 700, 700, 128, torch.bfloat16, seed=32, qk_mul=20.0)
+    for causal in (False, True):
+        o, lse = fa.fa_forward(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal)
+        torch.cuda.synchronize()
+        ro, rl = orc.attention(f64(q), f64(k), f64(v), 1.0 / math.sqrt(128), causal)
+        err_l = np.abs(f64(lse) - rl) / np.maximum(1.0, np.abs(rl))
+        print(f"[parity] huge scores causal={causal}: LSE rel max {err_l.max():.3e}", flush=True)
+        assert np.isfinite(f64(o)).all() and err_l.max() <= 1e-5
+        check_bf16(f"huge scores causal={causal}", o, lse, ro, f64(lse))
+
+
 # ---------------------------------------------------------------- closed forms and invariants on the GPU
 
 @pytest.mark.parametrize("D", [64, 128])
