@@ -1,7 +1,7 @@
 // bf16 FlashAttention forward for gfx950: MFMA for both contractions.
 //
 // Method (iThome FlashAttention article, "three states"; ML compiler page,
-// section 11.9): a workgroup owns BM = 128 query rows of one (batch, head) and
+// section 11.9): a workgroup owns BM = 256 query rows of one (batch, head) and
 // streams key/value tiles of BN keys past them. Per row it carries the running
 // maximum m, the running sum l and the unnormalised output O; for each tile
 //     m_new = max(m, rowmax S),  alpha = exp(m - m_new),  P = exp(S - m_new),
@@ -12,8 +12,9 @@
 // page, section 11.7), and LSE is converted back to natural log at the end.
 //
 // gfx950 mapping (own design):
-//   * 4 waves x 32 query rows. Q stays in VGPRs for the whole key loop as the B
-//     operand of v_mfma_f32_32x32x16_bf16.
+//   * 8 waves x 32 query rows, one workgroup per CU (2 waves per SIMD). Q stays
+//     in VGPRs for the whole key loop as the B operand of
+//     v_mfma_f32_32x32x16_bf16.
 //   * S is computed transposed, S^T = K Q^T (A = 32 keys of K from LDS), so that
 //     every lane ends with 16 scores of ONE query row: the row max / row sum are
 //     in-lane reductions plus one exchange with lane ^ 32.
@@ -23,16 +24,21 @@
 //     registers.
 //   * O^T lives in 16*D/32 fp32 accumulators per lane, one query row per lane,
 //     so the alpha rescale is a per-lane scalar multiply.
+//   * Ping-pong: every wave alternates an MFMA step (PV of the previous tile,
+//     then QK of the current one) and a softmax step, separated by workgroup
+//     barriers; the two wave groups (waves 0-3 and 4-7, one of each per SIMD)
+//     run a step apart, so on every SIMD one wave feeds the matrix core while
+//     the other runs the exponentials on the VALU.
 //   * K and V tiles go from global memory straight into LDS
-//     (global_load_lds_dwordx4: no VGPR staging), two tiles deep, one barrier
-//     per tile. Both are row-major in LDS with an XOR swizzle of their 16-byte
-//     chunks chosen so the MFMA operand reads are free of bank conflicts. The
-//     V^T operand (8 consecutive keys of one column per lane) is read with
-//     ds_read_b64_tr_b16, the LDS transpose read: within each 16-lane block,
-//     source lane s points at 4 consecutive columns of key k0 + s/4, and lane
-//     i receives column i of those 4 keys. Rows past Nk are clamped to the
-//     last key instead of branching: they are masked out of S, and their
-//     (finite) values are multiplied by P = 0.
+//     (global_load_lds_dwordx4: no VGPR staging), two tiles deep. Both are
+//     row-major in LDS with an XOR swizzle of their 16-byte chunks chosen so
+//     the MFMA operand reads are free of bank conflicts. The V^T operand (8
+//     consecutive keys of one column per lane) is read with ds_read_b64_tr_b16,
+//     the LDS transpose read: within each 16-lane block, source lane s points
+//     at 4 consecutive columns of key k0 + s/4, and lane i receives column i
+//     of those 4 keys. Rows past Nk are clamped to the last key instead of
+//     branching: they are masked out of S, and their (finite) values are
+//     multiplied by P = 0.
 //   * Conditional rescaling (the FA4 refinement the iThome article describes
 //     after the alpha derivation): the running maximum of a wave's rows is
 //     only moved, and O and l rescaled, when some row's tile maximum exceeds it
