@@ -40,6 +40,12 @@ What pins each function (tests/test_oracle.py):
 * ``merge`` / ``split_states`` / ``combine``: the numbers of the solution to
   exercise 3 (tests/golden/merge_example.json); every chunking of a row gives
   the two-pass answer.
+* ``attention_backward``: central finite differences of ``attention`` on tiny
+  inputs; torch's float64 CPU autograd through ``scaled_dot_product_attention``
+  as an independent library routine; closed forms (dO = 0 gives zero
+  gradients; equal V rows make O independent of Q and K, so dQ = dK = 0; the
+  rows of dK sum to zero and those of dV to the column sums of dO; the causal
+  row 0 sees one key, so its dQ is zero).
 """
 
 from __future__ import annotations
@@ -255,3 +261,48 @@ def decode(q, k, v, scale: float):
     no mask. The same definition as ``attention`` with Nq = 1; returns
     O [B, H, 1, D] and LSE [B, H, 1]."""
     return attention(q, k, v, scale, causal=False)
+
+
+# --------------------------------------------------------------------------
+# Backward pass (the exercise "Backward with recompute" of section 11: dQ, dK,
+# dV from O, dO and the saved log-sum-exp).
+# --------------------------------------------------------------------------
+
+def attention_backward_head(q, k, v, do, scale: float, causal: bool = False):
+    """Gradients of O = softmax(scale * Q K^T) V for one (batch, head).
+
+    q: [Nq, D], k, v: [Nk, D], do: [Nq, D] (the gradient of the loss with
+    respect to O). Returns (dQ, dK, dV) in float64.
+
+    The chain rule written out on the definition, the way the exercise asks
+    for it to be checked (against the gradient of the unfused graph):
+        P  = softmax(S),  S = scale * Q K^T (masked keys get P = 0)
+        dV = P^T dO
+        dP = dO V^T
+        dS = P * (dP - rowsum(P * dP))      (softmax Jacobian, row by row)
+        dQ = scale * dS K,   dK = scale * dS^T Q
+    rowsum(P * dP) equals rowsum(dO * O) because O = P V; the kernels use the
+    second form, this definition the first.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    p = softmax_weights(q, k, scale, causal)         # [Nq, Nk]
+    dv = p.T @ do
+    dp = do @ v.T
+    ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    dq = scale * (ds @ k)
+    dk = scale * (ds.T @ q)
+    return dq, dk, dv
+
+
+def attention_backward(q, k, v, do, scale: float, causal: bool = False):
+    """``attention_backward_head`` over [B, H, N, D] tensors; returns
+    (dQ, dK, dV) in float64 with the shapes of q, k, v."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    for bi in range(q.shape[0]):
+        for hi in range(q.shape[1]):
+            dq[bi, hi], dk[bi, hi], dv[bi, hi] = attention_backward_head(
+                q[bi, hi], k[bi, hi], v[bi, hi], do[bi, hi], scale, causal)
+    return dq, dk, dv

@@ -240,6 +240,81 @@ def pin_split_combine(orc):
         _close(lse, l_ref[0, 0, 0], 1e-13, f"split LSE S={splits}")
 
 
+# ---- backward pass ------------------------------------------------------------
+
+def pin_backward_finite_differences(orc):
+    """Central differences of the forward oracle: for L = sum(O * G), dL/dX from
+    (L(X + h E) - L(X - h E)) / 2h for every element of Q, K and V, against the
+    backward oracle (tiny shapes; causal and not; Nq != Nk)."""
+    h = 1e-6
+    for (nq, nk, d, causal, seed) in [(4, 4, 3, False, 40), (5, 5, 2, True, 41), (3, 6, 3, False, 42)]:
+        q = _rand((1, 1, nq, d), seed) * 1.5
+        k = _rand((1, 1, nk, d), seed + 1) * 1.5
+        v = _rand((1, 1, nk, d), seed + 2)
+        g = _rand((1, 1, nq, d), seed + 3)
+        scale = 0.6
+        dq, dk, dv = orc.attention_backward(q, k, v, g, scale, causal)
+
+        def loss(qq, kk, vv):
+            return float(np.sum(orc.attention(qq, kk, vv, scale, causal)[0] * g))
+
+        for name, x, grad in (("Q", q, dq), ("K", k, dk), ("V", v, dv)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(*x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                args_p = [q, k, v]
+                args_m = [q, k, v]
+                pos = "QKV".index(name)
+                args_p[pos], args_m[pos] = xp, xm
+                num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            _close(grad, num, 1e-7, f"finite differences d{name} {nq}x{nk} causal={causal}")
+
+
+def pin_backward_torch_autograd(orc):
+    """torch's float64 CPU autograd through scaled_dot_product_attention (an
+    independent library routine) agrees with the backward oracle."""
+    for (b, hh, nq, nk, d, causal, seed) in [(1, 2, 11, 11, 8, True, 43), (2, 1, 7, 13, 4, False, 44)]:
+        q = _rand((b, hh, nq, d), seed) * 2.0
+        k = _rand((b, hh, nk, d), seed + 1) * 2.0
+        v = _rand((b, hh, nk, d), seed + 2)
+        g = _rand((b, hh, nq, d), seed + 3)
+        scale = 1.0 / math.sqrt(d)
+        dq, dk, dv = orc.attention_backward(q, k, v, g, scale, causal)
+        tq, tk, tv = (torch.from_numpy(x).requires_grad_(True) for x in (q, k, v))
+        out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale)
+        out.backward(torch.from_numpy(g))
+        _close(dq, tq.grad.numpy(), 1e-12, f"autograd dQ causal={causal}")
+        _close(dk, tk.grad.numpy(), 1e-12, f"autograd dK causal={causal}")
+        _close(dv, tv.grad.numpy(), 1e-12, f"autograd dV causal={causal}")
+
+
+def pin_backward_closed_forms(orc):
+    """dO = 0 gives zero gradients; equal V rows make O independent of Q and K
+    (dQ = dK = 0); dK sums to zero over the keys (adding one vector to every
+    key shifts each row of S by a constant, which softmax ignores); dV sums
+    over the keys to the
+    column sums of dO (each row of P sums to one); the causal row 0 sees one
+    key, so its dQ is zero."""
+    q = _rand((1, 1, 9, 4), 45) * 2.0
+    k = _rand((1, 1, 9, 4), 46) * 2.0
+    v = _rand((1, 1, 9, 4), 47)
+    g = _rand((1, 1, 9, 4), 48)
+    for causal in (False, True):
+        dq, dk, dv = orc.attention_backward(q, k, v, np.zeros_like(g), 0.5, causal)
+        _close(np.abs(dq) + np.abs(dk) + np.abs(dv), np.zeros_like(q), 0.0, f"dO = 0 causal={causal}")
+        vconst = np.broadcast_to(_rand((1, 1, 1, 4), 49), v.shape).copy()
+        dq, dk, dv = orc.attention_backward(q, k, vconst, g, 0.5, causal)
+        _close(dq, np.zeros_like(dq), 1e-13, f"equal V rows dQ causal={causal}")
+        _close(dk, np.zeros_like(dk), 1e-13, f"equal V rows dK causal={causal}")
+        dq, dk, dv = orc.attention_backward(q, k, v, g, 0.5, causal)
+        _close(dk.sum(axis=2), np.zeros((1, 1, 4)), 1e-13, f"sum of dK causal={causal}")
+        _close(dv.sum(axis=2), g.sum(axis=2), 1e-13, f"sum of dV causal={causal}")
+        if causal:
+            _close(dq[0, 0, 0], np.zeros(4), 0.0, "causal row 0 dQ")
+
+
 ALL_PINS = [
     pin_worked_example_trace,
     pin_worked_example_two_pass,
@@ -255,4 +330,7 @@ ALL_PINS = [
     pin_online_blocked_matches,
     pin_online_per_key_matches,
     pin_split_combine,
+    pin_backward_finite_differences,
+    pin_backward_torch_autograd,
+    pin_backward_closed_forms,
 ]

@@ -25,6 +25,13 @@ MUTATIONS = {
     "merge_weight_sign": ("w1 = math.exp(m1 - m)", "w1 = math.exp(m - m1)"),
     "merge_drops_second_o": ("o1) * w1 + _f64(o2) * w2)", "o1) * w1)"),
     "chunk_floor": ("c = -(-nk // num_splits)", "c = max(1, nk // num_splits)"),
+    "bwd_dv_untransposed": ("dv = p.T @ do", "dv = p @ do"),
+    "bwd_dp_wrong_operand": ("dp = do @ v.T", "dp = do @ k.T"),
+    "bwd_softmax_jacobian_sign": ("ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))",
+                                  "ds = p * (dp + (p * dp).sum(axis=1, keepdims=True))"),
+    "bwd_softmax_jacobian_dropped": ("ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))", "ds = p * dp"),
+    "bwd_dq_no_scale": ("dq = scale * (ds @ k)", "dq = ds @ k"),
+    "bwd_dk_wrong_operand": ("dk = scale * (ds.T @ q)", "dk = scale * (ds.T @ k)"),
 }
 
 
