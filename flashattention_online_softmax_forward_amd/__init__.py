@@ -22,6 +22,8 @@ __all__ = [
     "fa_forward_f32",
     "fa_decode_splitkv",
     "fa_decode_workspace_bytes",
+    "fa_backward",
+    "fa_backward_workspace_bytes",
     "fa_status_string",
     "FAError",
 ]
@@ -135,3 +137,52 @@ def fa_decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, num_spl
         B, H, Nk, D, float(scale), int(num_splits), _stream(q))
     _lib.check(code, "fa_decode_splitkv")
     return out, lse
+
+
+def fa_backward_workspace_bytes(B: int, H: int, Nq: int) -> int:
+    return int(_lib.load().fa_backward_workspace_bytes(B, H, Nq))
+
+
+def fa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                do: torch.Tensor, lse: torch.Tensor, causal: bool = False,
+                scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
+                dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                dv: Optional[torch.Tensor] = None
+                ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """bf16 backward with recompute: q, o, do [B,H,Nq,D], k, v [B,H,Nk,D], lse
+    fp32 [B,H,Nq] (the forward's, same scale and causal flag). Returns
+    (dQ, dK, dV) in bf16 with the shapes of q, k, v. ``workspace`` holds at
+    least fa_backward_workspace_bytes(B,H,Nq) bytes; one is allocated when not
+    given."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check_tensor(name, t, torch.bfloat16)
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    if tuple(k.shape) != (B, H, Nk, D) or tuple(v.shape) != (B, H, Nk, D):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if tuple(o.shape) != tuple(q.shape) or tuple(do.shape) != tuple(q.shape):
+        raise ValueError("o and do must have q's shape")
+    _check_tensor("lse", lse, torch.float32, ndim=3)
+    if tuple(lse.shape) != (B, H, Nq):
+        raise ValueError("lse must be [B, H, Nq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = fa_backward_workspace_bytes(B, H, Nq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check_tensor(name, t, torch.bfloat16)
+        if tuple(t.shape) != tuple(ref.shape):
+            raise ValueError(f"{name} must have the shape {tuple(ref.shape)}")
+    code = _lib.load().fa_backward(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), ws_bytes,
+        B, H, Nq, Nk, D, float(scale), int(bool(causal)), _stream(q))
+    _lib.check(code, "fa_backward")
+    return dq, dk, dv

@@ -18,6 +18,8 @@ PROTOTYPES = {
     "fa_forward_f32": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp]),
     "fa_decode_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "fa_decode_splitkv": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _i, _i, _i, _i, _f, _i, _vp]),
+    "fa_backward_workspace_bytes": (_sz, [_i, _i, _i]),
+    "fa_backward": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i, _i, _i, _i, _i, _f, _i, _vp]),
     "fa_status_string": (ctypes.c_char_p, [_i]),
 }
 

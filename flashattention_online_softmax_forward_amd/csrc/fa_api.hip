@@ -116,4 +116,54 @@ fa_status fa_decode_splitkv(const void* Q, const void* K, const void* V, void* O
     return fa::launch_decode(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+size_t fa_backward_workspace_bytes(int B, int H, int Nq) {
+    if (B < 0 || H < 0 || Nq < 0) return 0;
+    return (size_t)B * H * Nq * sizeof(float);
+}
+
+fa_status fa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                      const float* LSE, void* dQ, void* dK, void* dV, void* workspace,
+                      size_t workspace_bytes, int B, int H, int Nq, int Nk, int D, float scale,
+                      int causal, hipStream_t stream) {
+    if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return FA_ERR_INVALID_ARG;
+    if (!good_scale(scale)) return FA_ERR_INVALID_ARG;
+    if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * H == 0 || ((long long)Nq == 0 && Nk == 0)) return FA_OK;
+    if (Nk < 1) return FA_ERR_INVALID_ARG;
+    const long long nkb = ((long long)Nk + fa::BM_BWD - 1) / fa::BM_BWD;
+    if ((long long)B * H * nkb > INT_MAX) return FA_ERR_UNSUPPORTED;
+    const size_t bkv = (size_t)B * H * Nk * D * 2;
+    if (Nq == 0) {
+        // No query reads any key: dK = dV = 0 (only K, V, dK, dV are used).
+        if (!dK || !dV || !aligned16(dK) || !aligned16(dV)) return FA_ERR_INVALID_ARG;
+        if (overlaps(dK, bkv, dV, bkv) || overlaps(dK, bkv, K, bkv) || overlaps(dK, bkv, V, bkv) ||
+            overlaps(dV, bkv, K, bkv) || overlaps(dV, bkv, V, bkv))
+            return FA_ERR_INVALID_ARG;
+    } else {
+        if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV || !workspace) return FA_ERR_INVALID_ARG;
+        if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) ||
+            !aligned16(dQ) || !aligned16(dK) || !aligned16(dV) || !aligned16(workspace) || !aligned4(LSE))
+            return FA_ERR_INVALID_ARG;
+        const long long nqb = ((long long)Nq + fa::BM_BWD - 1) / fa::BM_BWD;
+        if ((long long)B * H * nqb > INT_MAX || (long long)B * H * Nq > INT_MAX) return FA_ERR_UNSUPPORTED;
+        const size_t need = fa_backward_workspace_bytes(B, H, Nq);
+        if (workspace_bytes < need) return FA_ERR_INVALID_ARG;
+        const size_t bq = (size_t)B * H * Nq * D * 2;
+        const size_t bl = (size_t)B * H * Nq * sizeof(float);
+        const void* ins[6] = {Q, K, V, O, dO, LSE};
+        const size_t in_bytes[6] = {bq, bkv, bkv, bq, bq, bl};
+        const void* outs[4] = {dQ, dK, dV, workspace};
+        const size_t out_bytes[4] = {bq, bkv, bkv, need};
+        for (int i = 0; i < 4; ++i) {
+            for (int j = 0; j < 6; ++j)
+                if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return FA_ERR_INVALID_ARG;
+            for (int j = i + 1; j < 4; ++j)
+                if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return FA_ERR_INVALID_ARG;
+        }
+    }
+    const fa::BwdArgs a{Q, K, V, O, dO, LSE, dQ, dK, dV, static_cast<float*>(workspace),
+                        B, H, Nq, Nk, D, scale, causal != 0, stream};
+    return fa::launch_bwd(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -1,0 +1,564 @@
+// Backward pass with recompute for gfx950 ("Backward with recompute" exercise
+// and section 11.9 of the ML compiler page: only O and the per-row
+// log-sum-exp L are kept from the forward pass; P is recomputed block by block
+// as exp(S - L)). For one (batch, head):
+//     D_i = sum_d dO[i,d] O[i,d]                       (bwd_rowdot_kernel)
+//     P = exp(scale Q K^T - L),  dP = dO V^T,  dS = P * (dP - D)
+//     dQ = scale dS K                                  (bwd_dq_kernel)
+//     dV = P^T dO,  dK = scale dS^T Q                  (bwd_dkdv_kernel)
+// Exponentials are base 2 (scale and L multiplied by log2 e).
+//
+// gfx950 mapping (own design, on the forward kernel's MFMA layouts):
+//   * Both product kernels use v_mfma_f32_32x32x16_bf16 with 4 waves x 32
+//     rows per workgroup and stream the other operand through LDS in tiles of
+//     32 rows (global_load_lds_dwordx4 DMA, double-buffered, one barrier per
+//     tile).
+//   * dQ: a wave owns 32 query rows; Q and dO stay in VGPRs as B operands.
+//     S^T = K Q^T and dP^T = V dO^T put one query per lane, so L and D are
+//     per-lane scalars. The rows of K and V fed to the A operand are permuted
+//     (bits 2 and 3 of the row swapped) so the accumulator of dS^T, rounded to
+//     bf16, is directly the B operand of dQ^T += K^T dS^T; K^T is read from
+//     the same LDS tile with ds_read_b64_tr_b16.
+//   * dK, dV: a wave owns 32 keys; K stays in VGPRs and the workgroup's 128
+//     V rows in LDS (both as B operands). S = Q K^T and dP = dO V^T put one
+//     key per lane (L and D, per query, come from LDS); P and dS, rounded to
+//     bf16, are the B operands of dV^T += dO^T P and dK^T += Q^T dS, whose A
+//     operands are transpose reads of the Q and dO tiles.
+//   * Every tile is read both row-wise (16-byte MFMA operand rows) and
+//     transposed (8-byte transpose reads of 4 consecutive rows). One XOR
+//     swizzle of the 16-byte chunks makes both patterns free of LDS bank
+//     conflicts, so each tile is staged once.
+//   * Masking: causal (key j visible from query i iff j <= i), keys past Nk
+//     and queries past Nq get P = 0 (so dS = 0 too); rows past the end are
+//     loaded clamped to the last row and never stored.
+//   * dQ, dK, dV are accumulated in fp32 and rounded to bf16 once.
+
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdThreads = 64 * kBwdWaves;
+constexpr int kBT = 32;                    // rows per streamed tile
+static_assert(BM_BWD == 32 * kBwdWaves, "32 rows per wave");
+
+#define LDS_AS __attribute__((address_space(3)))
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+// Lane-row i of an MFMA A operand reads tile row perm(i) (bits 2 and 3
+// swapped): accumulator register r of lane (j, h) then holds row
+// 16*(r/8) + 8*h + (r%8), 8 consecutive rows per lane half.
+__device__ __forceinline__ int row_perm(int i) {
+    return (i & ~0xC) | ((i & 4) << 1) | ((i & 8) >> 1);
+}
+
+// 16-byte chunk swizzle of a row of CPR chunks, conflict-free both for 16
+// lanes reading 16 different rows at one chunk and for transpose reads of 4
+// consecutive rows x 4 chunks (checked bank by bank on the host).
+template <int CPR>
+__device__ __forceinline__ int swz(int row) {
+    return CPR == 16 ? (((row & 3) << 2) | ((row >> 2) & 3))
+                     : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
+
+// One global_load_lds_dwordx4: every lane copies 16 bytes from base + voff to
+// LDS address lds + 16 * lane (lds is wave-uniform, in M0). Inline asm keeps
+// it out of the compiler's wait-count bookkeeping; the kernels wait for their
+// loads themselves before the barrier that publishes them.
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma_wait_all() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
+    return (uint32_t)(uintptr_t)(LDS_AS const uint16_t*)p;
+}
+
+// Stage `rows` rows (a multiple of 32) of a row-major [*, D] bf16 array into
+// LDS with the chunk swizzle: chunk p of the tile lands at byte 16*p and holds
+// logical chunk (p % CPR) ^ swz(row) of row p / CPR. Rows past `last` (the
+// last valid row, relative to src) are clamped to it.
+template <int D>
+__device__ __forceinline__ void stage_rows(const uint16_t* src, int rows, int last, uint16_t* dst,
+                                           int wave, int lane) {
+    constexpr int CPR = D / 8;
+    const int per = rows * CPR / kBwdThreads;          // chunks per thread
+    for (int i = 0; i < per; ++i) {
+        const int p = (i * kBwdWaves + wave) * 64 + lane;
+        const int row = p / CPR;
+        const int rr = row < last ? row : last;
+        const uint32_t off = (uint32_t)(rr * D + ((p % CPR) ^ swz<CPR>(row)) * 8) * 2u;
+        lds_dma16(src, off, lds_addr(dst + (i * kBwdWaves + wave) * 512));
+    }
+}
+
+// Lane-dependent LDS byte offsets of the MFMA operand reads of a staged
+// 32-row tile. They are the same for every tile buffer (the buffer's base is
+// a compile-time constant that folds into the instruction's offset field),
+// computed once and pinned in VGPRs.
+//   row[kk]: A operand rows, lane (j, h) reads row row_perm(j), elements
+//            16*kk + 8*h .. +7.
+//   tr[2*db + rd]: A operand transposed, element (i, k) = tile[16*tt + k]
+//            [32*db + i], two transpose reads rd = 0, 1 (rows 16*tt + 8*h +
+//            4*rd + s/4 for source lane s of each 16-lane block, 4 columns
+//            from 32*db + 16*(lane/16 % 2) + 4*(s%4)); add 16*tt rows.
+template <int D>
+struct TileOffsets {
+    uint32_t row[D / 16];
+    uint32_t tr[2 * (D / 32)];
+    __device__ __forceinline__ void init(int lane) {
+        constexpr int CPR = D / 8;
+        const int j = lane & 31, h = lane >> 5, blk = (lane >> 4) & 1, v_s = lane & 15;
+        const int r = row_perm(j);
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            row[kk] = (uint32_t)(r * D + ((kk * 2 + h) ^ swz<CPR>(r)) * 8) * 2u;
+            asm volatile("" : "+v"(row[kk]));
+        }
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int rd = 0; rd < 2; ++rd) {
+                const int rr = h * 8 + rd * 4 + (v_s >> 2);
+                const int col = db * 32 + blk * 16 + (v_s & 3) * 4;
+                tr[db * 2 + rd] = (uint32_t)(rr * D + ((col >> 3) ^ swz<CPR>(rr)) * 8 + (col & 7)) * 2u;
+                asm volatile("" : "+v"(tr[db * 2 + rd]));
+            }
+    }
+};
+
+template <int D>
+__device__ __forceinline__ bf16x8_t row_operand(const uint16_t* tile, const TileOffsets<D>& o, int kk) {
+    return *(LDS_AS const bf16x8_t*)((LDS_AS const char*)(LDS_AS const uint16_t*)tile + o.row[kk]);
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8_t tr_operand(const uint16_t* tile, const TileOffsets<D>& o, int tt, int db) {
+    bf16x4_t part[2];
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd)
+        part[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (LDS_AS bf16x4_t*)((LDS_AS char*)(LDS_AS uint16_t*)tile + o.tr[db * 2 + rd] + (uint32_t)(tt * 16 * D * 2)));
+    return bf16x8_t{part[0][0], part[0][1], part[0][2], part[0][3],
+                    part[1][0], part[1][1], part[1][2], part[1][3]};
+}
+
+// Row `row` of a [*, D] array as MFMA B operands: lane (j, h) holds elements
+// 16*kk + 8*h .. +7 (zero when the row is past the end).
+template <int D>
+__device__ __forceinline__ void load_b_rows(const uint16_t* base, int row, bool valid, int h, bf16x8_t* out) {
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+        u32x4_t w = {0u, 0u, 0u, 0u};
+        if (valid) w = *(const u32x4_t*)(base + (size_t)row * D + kk * 16 + h * 8);
+        out[kk] = __builtin_bit_cast(bf16x8_t, w);
+    }
+}
+
+// Store an fp32 accumulator of 32 rows x D held transposed (lane j = row,
+// register r of block db = column 32*db + 8*(r/4) + 4*h + r%4) as bf16,
+// multiplied by `mul`.
+template <int D>
+__device__ __forceinline__ void store_rows(uint16_t* rowp, const f32x16_t* acc, int h, float mul) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+            const int d = db * 32 + a4 * 8 + h * 4;
+            u32x2_t w;
+            w[0] = pack_bf16x2(acc[db][a4 * 4 + 0] * mul, acc[db][a4 * 4 + 1] * mul);
+            w[1] = pack_bf16x2(acc[db][a4 * 4 + 2] * mul, acc[db][a4 * 4 + 3] * mul);
+            *(u32x2_t*)(rowp + d) = w;
+        }
+}
+
+// N MFMAs acc[dst(i)] += op(i) x b(i), each A operand read LEAD MFMAs ahead
+// and no further (sched_barrier after every step), which bounds the operand
+// registers a phase holds.
+template <int N, int LEAD, typename Op, typename Step>
+__device__ __forceinline__ void mfma_stream(Op op, Step step) {
+    bf16x8_t ring[LEAD];
+#pragma unroll
+    for (int i = 0; i < LEAD && i < N; ++i) ring[i] = op(i);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const bf16x8_t a = ring[i % LEAD];
+        if (i + LEAD < N) ring[i % LEAD] = op(i + LEAD);
+        step(i, a);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+}  // namespace
+
+// D_i = sum_d dO[i,d] O[i,d] in fp32: D/8 lanes per row, 8 elements each.
+template <int D>
+__global__ __launch_bounds__(256)
+void bwd_rowdot_kernel(const uint16_t* __restrict__ Og, const uint16_t* __restrict__ dOg,
+                       float* __restrict__ Dg, long long rows) {
+    constexpr int LPR = D / 8;
+    constexpr int RPB = 256 / LPR;
+    const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
+    const int sub = threadIdx.x % LPR;
+    float acc = 0.f;
+    if (row < rows) {
+        const u32x4_t a = *(const u32x4_t*)(Og + row * D + sub * 8);
+        const u32x4_t b = *(const u32x4_t*)(dOg + row * D + sub * 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc = __builtin_fmaf(bf16_lo(a[i]), bf16_lo(b[i]), acc);
+            acc = __builtin_fmaf(bf16_hi(a[i]), bf16_hi(b[i]), acc);
+        }
+    }
+    acc = group_sum<LPR>(acc);
+    if (row < rows && sub == 0) Dg[row] = acc;
+}
+
+// dQ for 128 query rows of one (batch, head), streaming K and V tiles.
+template <int D>
+__global__ __launch_bounds__(kBwdThreads, 2)
+void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
+                   const uint16_t* __restrict__ Vg, const uint16_t* __restrict__ dOg,
+                   const float* __restrict__ LSEg, const float* __restrict__ Dg,
+                   uint16_t* __restrict__ dQg, int Nq, int Nk, int nqb, float scale, float scale2,
+                   int causal) {
+    constexpr int NKK = D / 16, NDB = D / 32;
+    constexpr int TILE = kBT * D;
+    const bool CAUSAL = causal != 0;
+
+    __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[TILE];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int j = lane & 31;
+    const int h = lane >> 5;
+
+    const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int bh = logical / nqb;
+    int qb = logical - bh * nqb;
+    if (CAUSAL) qb = nqb - 1 - qb;             // longest rows first
+    const int q0 = qb * BM_BWD;
+    const int wrow0 = q0 + wave * 32;
+    const int qrow = wrow0 + j;
+    const bool qvalid = qrow < Nq;
+
+    const uint16_t* K = Kg + (size_t)bh * Nk * D;
+    const uint16_t* V = Vg + (size_t)bh * Nk * D;
+
+    bf16x8_t qf[NKK], dof[NKK];
+    load_b_rows<D>(Qg + (size_t)bh * Nq * D, qrow, qvalid, h, qf);
+    load_b_rows<D>(dOg + (size_t)bh * Nq * D, qrow, qvalid, h, dof);
+    const float l2 = qvalid ? LSEg[(size_t)bh * Nq + qrow] * kLog2e : 0.f;
+    const float dr = qvalid ? Dg[(size_t)bh * Nq + qrow] : 0.f;
+
+    TileOffsets<D> off;
+    off.init(lane);
+
+    f32x16_t acc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+
+    int kend = Nk;
+    if (CAUSAL) kend = min(Nk, min(q0 + BM_BWD, Nq));
+    const int ntiles = (kend + kBT - 1) / kBT;
+    const int my_tiles = CAUSAL ? min(ntiles, (wrow0 + 31) / kBT + 1) : ntiles;
+
+    auto stage = [&](int t, uint16_t* kd, uint16_t* vd) __attribute__((always_inline)) {
+        const int kv0 = t * kBT;
+        stage_rows<D>(K + (size_t)kv0 * D, kBT, Nk - 1 - kv0, kd, wave, lane);
+        stage_rows<D>(V + (size_t)kv0 * D, kBT, Nk - 1 - kv0, vd, wave, lane);
+    };
+    auto compute = [&](int t, const uint16_t* kt, const uint16_t* vt) __attribute__((always_inline)) {
+        // S^T = K Q^T and dP^T = V dO^T for 32 keys x this wave's 32 queries.
+        f32x16_t s = {}, dp = {};
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(kt, off, kk), qf[kk], s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(vt, off, kk), dof[kk], dp, 0, 0, 0);
+        }
+        const int kv0 = t * kBT;
+        const bool edge = kv0 + kBT > Nk || (CAUSAL && kv0 + kBT - 1 > wrow0);
+        bf16x8_t dsf[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            float ds[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int r = tt * 8 + e;
+                float p = exp2_hw(__builtin_fmaf(s[r], scale2, -l2));
+                if (edge) {
+                    const int key = kv0 + tt * 16 + h * 8 + e;
+                    if (key >= Nk || (CAUSAL && key > qrow)) p = 0.f;
+                }
+                ds[e] = p * (dp[r] - dr);
+            }
+            u32x4_t w;
+            w[0] = pack_bf16x2(ds[0], ds[1]);
+            w[1] = pack_bf16x2(ds[2], ds[3]);
+            w[2] = pack_bf16x2(ds[4], ds[5]);
+            w[3] = pack_bf16x2(ds[6], ds[7]);
+            dsf[tt] = __builtin_bit_cast(bf16x8_t, w);
+        }
+        // dQ^T += K^T dS^T.
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(kt, off, tt, db), dsf[tt], acc[db], 0, 0, 0);
+    };
+
+    stage(0, k_lds0, v_lds0);
+    lds_dma_wait_all();
+    __syncthreads();
+    // Tile t in buffer t % 2; the next tile is loaded while t is computed and
+    // published by the barrier that ends the iteration.
+    for (int t = 0; t < ntiles; t += 2) {
+        if (t + 1 < ntiles) stage(t + 1, k_lds1, v_lds1);
+        if (t < my_tiles) compute(t, k_lds0, v_lds0);
+        lds_dma_wait_all();
+        __syncthreads();
+        if (t + 1 >= ntiles) break;
+        if (t + 2 < ntiles) stage(t + 2, k_lds0, v_lds0);
+        if (t + 1 < my_tiles) compute(t + 1, k_lds1, v_lds1);
+        lds_dma_wait_all();
+        __syncthreads();
+    }
+
+    if (qvalid) store_rows<D>(dQg + ((size_t)bh * Nq + qrow) * D, acc, h, scale);
+}
+
+// dK and dV for 128 keys of one (batch, head), streaming Q, dO, L and D tiles.
+template <int D>
+__global__ __launch_bounds__(kBwdThreads, 2)
+void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
+                     const uint16_t* __restrict__ Vg, const uint16_t* __restrict__ dOg,
+                     const float* __restrict__ LSEg, const float* __restrict__ Dg,
+                     uint16_t* __restrict__ dKg, uint16_t* __restrict__ dVg, int Nq, int Nk, int nkb,
+                     float scale, float scale2, int causal) {
+    constexpr int NKK = D / 16, NDB = D / 32, CPR = D / 8;
+    constexpr int TILE = kBT * D;
+    const bool CAUSAL = causal != 0;
+
+    // Small arrays first: every buffer's base then fits the 16-bit offset
+    // field of the LDS instructions.
+    __shared__ __attribute__((aligned(16))) float ld_lds[2][2 * kBT];  // per tile: L (base 2), then D
+    __shared__ __attribute__((aligned(1024))) uint16_t q_lds0[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t q_lds1[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t o_lds0[TILE];    // dO tiles
+    __shared__ __attribute__((aligned(1024))) uint16_t o_lds1[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_blk[BM_BWD * D];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int j = lane & 31;
+    const int h = lane >> 5;
+
+    const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int bh = logical / nkb;
+    const int kb = logical - bh * nkb;         // causal: low key blocks carry the most queries
+    const int k0 = kb * BM_BWD;
+    const int kw0 = k0 + wave * 32;
+    const int krow = kw0 + j;
+    const bool kvalid = krow < Nk;
+
+    const uint16_t* Q = Qg + (size_t)bh * Nq * D;
+    const uint16_t* dO = dOg + (size_t)bh * Nq * D;
+    const float* L = LSEg + (size_t)bh * Nq;
+    const float* Dv = Dg + (size_t)bh * Nq;
+
+    bf16x8_t kf[NKK];
+    load_b_rows<D>(Kg + (size_t)bh * Nk * D, krow, kvalid, h, kf);
+    TileOffsets<D> off;
+    off.init(lane);
+    // V rows of this wave as MFMA B operands of dP = dO V^T: lane (j, h)
+    // reads row 32*wave + j of the block, elements 16*kk + 8*h .. +7.
+    uint32_t voff[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+        const int row = wave * 32 + j;
+        voff[kk] = (uint32_t)(row * D + ((kk * 2 + h) ^ swz<CPR>(row)) * 8) * 2u;
+        asm volatile("" : "+v"(voff[kk]));
+    }
+
+    f32x16_t adk[NDB], adv[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            adk[db][r] = 0.f;
+            adv[db][r] = 0.f;
+        }
+
+    const int nqt = (Nq + kBT - 1) / kBT;
+    // Causal: queries i >= key j only, so tiles start at the block's (the
+    // wave's) first key.
+    const int first = CAUSAL ? min(nqt, k0 / kBT) : 0;
+    const int my_first = CAUSAL ? min(nqt, kw0 / kBT) : 0;
+
+    // L and D of tile u through registers of wave 0 (lanes 0-31: L, 32-63: D).
+    float ld_reg = 0.f;
+    auto fetch_ld = [&](int u) __attribute__((always_inline)) {
+        if (wave == 0) {
+            const int q = min(u * kBT + j, Nq - 1);
+            ld_reg = h == 0 ? L[q] * kLog2e : Dv[q];
+        }
+    };
+    auto put_ld = [&](int buf) __attribute__((always_inline)) {
+        if (wave == 0) ld_lds[buf][lane] = ld_reg;
+    };
+    auto stage = [&](int u, uint16_t* qd, uint16_t* od) __attribute__((always_inline)) {
+        const int q0 = u * kBT;
+        stage_rows<D>(Q + (size_t)q0 * D, kBT, Nq - 1 - q0, qd, wave, lane);
+        stage_rows<D>(dO + (size_t)q0 * D, kBT, Nq - 1 - q0, od, wave, lane);
+    };
+    auto v_operand = [&](int kk) __attribute__((always_inline)) {
+        return *(LDS_AS const bf16x8_t*)((LDS_AS const char*)(LDS_AS const uint16_t*)v_blk + voff[kk]);
+    };
+    // One tile in phases with their own live registers (sched_barrier between
+    // them): S = Q K^T, P, dV^T += dO^T P, dP = dO V^T, dS, dK^T += Q^T dS.
+    auto compute = [&](int u, const uint16_t* qt, const uint16_t* ot, int buf) __attribute__((always_inline)) {
+        constexpr int LEAD = 2;
+        f32x16_t s = {};
+        mfma_stream<NKK, LEAD>([&](int kk) { return row_operand<D>(qt, off, kk); },
+                               [&](int kk, bf16x8_t a) { s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[kk], s, 0, 0, 0); });
+        const int q0 = u * kBT;
+        const bool edge = q0 + kBT > Nq || (CAUSAL && q0 < kw0 + 31);
+        // P (fp32, kept for dS) and its bf16 copy. Register r of lane (j, h)
+        // is query 16*(r/8) + 8*h + r%8 of the tile.
+        bf16x8_t pf[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const f32x4_t la = *(const f32x4_t*)&ld_lds[buf][tt * 16 + h * 8];
+            const f32x4_t lb = *(const f32x4_t*)&ld_lds[buf][tt * 16 + h * 8 + 4];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int r = tt * 8 + e;
+                float p = exp2_hw(__builtin_fmaf(s[r], scale2, -(e < 4 ? la[e] : lb[e - 4])));
+                if (edge) {
+                    const int q = q0 + tt * 16 + h * 8 + e;
+                    if (q >= Nq || (CAUSAL && q < krow)) p = 0.f;
+                }
+                s[r] = p;
+            }
+            u32x4_t w;
+            w[0] = pack_bf16x2(s[tt * 8 + 0], s[tt * 8 + 1]);
+            w[1] = pack_bf16x2(s[tt * 8 + 2], s[tt * 8 + 3]);
+            w[2] = pack_bf16x2(s[tt * 8 + 4], s[tt * 8 + 5]);
+            w[3] = pack_bf16x2(s[tt * 8 + 6], s[tt * 8 + 7]);
+            pf[tt] = __builtin_bit_cast(bf16x8_t, w);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_stream<2 * NDB, LEAD>([&](int i) { return tr_operand<D>(ot, off, i / NDB, i % NDB); },
+                                   [&](int i, bf16x8_t a) {
+                                       adv[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[i / NDB], adv[i % NDB], 0, 0, 0);
+                                   });
+        f32x16_t dp = {};
+        mfma_stream<NKK, LEAD>([&](int kk) { return row_operand<D>(ot, off, kk); },
+                               [&](int kk, bf16x8_t a) {
+                                   dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, v_operand(kk), dp, 0, 0, 0);
+                               });
+        bf16x8_t dsf[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const f32x4_t da = *(const f32x4_t*)&ld_lds[buf][kBT + tt * 16 + h * 8];
+            const f32x4_t dbv = *(const f32x4_t*)&ld_lds[buf][kBT + tt * 16 + h * 8 + 4];
+            float ds[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int r = tt * 8 + e;
+                ds[e] = s[r] * (dp[r] - (e < 4 ? da[e] : dbv[e - 4]));
+            }
+            u32x4_t x;
+            x[0] = pack_bf16x2(ds[0], ds[1]);
+            x[1] = pack_bf16x2(ds[2], ds[3]);
+            x[2] = pack_bf16x2(ds[4], ds[5]);
+            x[3] = pack_bf16x2(ds[6], ds[7]);
+            dsf[tt] = __builtin_bit_cast(bf16x8_t, x);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_stream<2 * NDB, LEAD>([&](int i) { return tr_operand<D>(qt, off, i / NDB, i % NDB); },
+                                   [&](int i, bf16x8_t a) {
+                                       adk[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsf[i / NDB], adk[i % NDB], 0, 0, 0);
+                                   });
+    };
+
+    // Prologue: the block's V rows (clamped to the last key) and the first tile.
+    stage_rows<D>(Vg + ((size_t)bh * Nk + k0) * D, BM_BWD, Nk - 1 - k0, v_blk, wave, lane);
+    if (first < nqt) {
+        stage(first, q_lds0, o_lds0);
+        fetch_ld(first);
+        put_ld(0);
+    }
+    lds_dma_wait_all();
+    __syncthreads();
+    // Tile first + 2i in buffer 0, first + 2i + 1 in buffer 1.
+    for (int u = first; u < nqt; u += 2) {
+        if (u + 1 < nqt) {
+            stage(u + 1, q_lds1, o_lds1);
+            fetch_ld(u + 1);
+        }
+        if (u >= my_first) compute(u, q_lds0, o_lds0, 0);
+        if (u + 1 < nqt) put_ld(1);
+        lds_dma_wait_all();
+        __syncthreads();
+        if (u + 1 >= nqt) break;
+        if (u + 2 < nqt) {
+            stage(u + 2, q_lds0, o_lds0);
+            fetch_ld(u + 2);
+        }
+        if (u + 1 >= my_first) compute(u + 1, q_lds1, o_lds1, 1);
+        if (u + 2 < nqt) put_ld(0);
+        lds_dma_wait_all();
+        __syncthreads();
+    }
+
+    if (kvalid) {
+        store_rows<D>(dKg + ((size_t)bh * Nk + krow) * D, adk, h, scale);
+        store_rows<D>(dVg + ((size_t)bh * Nk + krow) * D, adv, h, 1.0f);
+    }
+}
+
+template <int D>
+static hipError_t launch_bwd_d(const BwdArgs& a) {
+    const float scale2 = a.scale * kLog2e;
+    if (a.Nq > 0) {
+        const long long rows = (long long)a.B * a.H * a.Nq;
+        constexpr int RPB = 256 / (D / 8);
+        hipLaunchKernelGGL((bwd_rowdot_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
+                           a.stream, (const uint16_t*)a.O, (const uint16_t*)a.dO, a.Dvec, rows);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int nqb = (a.Nq + BM_BWD - 1) / BM_BWD;
+        hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3(a.B * a.H * nqb), dim3(kBwdThreads), 0, a.stream,
+                           (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
+                           (const uint16_t*)a.dO, a.LSE, a.Dvec, (uint16_t*)a.dQ, a.Nq, a.Nk, nqb,
+                           a.scale, scale2, a.causal);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    // With Nq = 0 the dK/dV kernel stages only V, runs no query tile and
+    // stores zeros.
+    const int nkb = (a.Nk + BM_BWD - 1) / BM_BWD;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(a.B * a.H * nkb), dim3(kBwdThreads), 0, a.stream,
+                       (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
+                       (const uint16_t*)a.dO, a.LSE, a.Dvec, (uint16_t*)a.dK, (uint16_t*)a.dV,
+                       a.Nq, a.Nk, nkb, a.scale, scale2, a.causal);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdArgs& a) {
+    return a.D == 128 ? launch_bwd_d<128>(a) : launch_bwd_d<64>(a);
+}
+
+}  // namespace fa

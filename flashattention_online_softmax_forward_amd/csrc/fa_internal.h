@@ -8,6 +8,7 @@ namespace fa {
 
 constexpr int BM_FWD = 256;      // query rows per workgroup, bf16 forward (8 waves x 32)
 constexpr int BM_FWD_F32 = 64;   // query rows per workgroup, fp32 forward
+constexpr int BM_BWD = 128;      // rows (queries for dQ, keys for dK/dV) per workgroup, backward (4 waves x 32)
 
 struct FwdArgs {
     const void* Q;
@@ -34,8 +35,26 @@ struct DecodeArgs {
     hipStream_t stream;
 };
 
+struct BwdArgs {
+    const void* Q;
+    const void* K;
+    const void* V;
+    const void* O;
+    const void* dO;
+    const float* LSE;
+    void* dQ;
+    void* dK;
+    void* dV;
+    float* Dvec;     // [B*H, Nq] row dot products sum_d dO * O
+    int B, H, Nq, Nk, D;
+    float scale;
+    int causal;
+    hipStream_t stream;
+};
+
 hipError_t launch_fwd_bf16(const FwdArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_bwd(const BwdArgs& a);
 
 }  // namespace fa

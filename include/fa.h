@@ -1,5 +1,6 @@
 /*
- * fa.h — C ABI of the MI355X (gfx950) FlashAttention forward library.
+ * fa.h — C ABI of the MI355X (gfx950) FlashAttention library: forward pass,
+ * split-KV decode and backward pass.
  *
  * The operation (the same for every entry point) is exact softmax attention
  *     O[b,h,i,:] = sum_j softmax_j(scale * Q[b,h,i,:] . K[b,h,j,:]) * V[b,h,j,:]
@@ -103,6 +104,44 @@ fa_status fa_decode_splitkv(const void* Q, const void* K, const void* V,
                             void* workspace, size_t workspace_bytes,
                             int B, int H, int Nk, int D,
                             float scale, int num_splits, hipStream_t stream);
+
+/*
+ * Bytes of device workspace fa_backward needs: B*H*Nq*4 (one fp32 value per
+ * query row, D_i = sum_d dO[i,d] * O[i,d]). Returns 0 for invalid arguments.
+ */
+size_t fa_backward_workspace_bytes(int B, int H, int Nq);
+
+/*
+ * Backward pass with recompute: the gradients dQ, dK, dV of a loss whose
+ * gradient with respect to O is dO, for the forward pass fa_forward computed
+ * ("Backward with recompute" exercise and section 11.9 of the ML compiler
+ * page: only O and the per-row log-sum-exp are kept from the forward pass;
+ * the probabilities are recomputed block by block as P = exp(S - LSE)).
+ *     dV = P^T dO,   dP = dO V^T,   D_i = sum_d dO[i,d] O[i,d],
+ *     dS = P * (dP - D),   dQ = scale * dS K,   dK = scale * dS^T Q.
+ *   Q, O, dO: bf16 [B,H,Nq,D]; K, V: bf16 [B,H,Nk,D]; LSE: fp32 [B,H,Nq], the
+ *   natural-log values fa_forward wrote for the same Q, K, V, scale and causal
+ *   (required, not NULL); dQ: bf16 [B,H,Nq,D]; dK, dV: bf16 [B,H,Nk,D]
+ *   (written; fully overwritten).
+ *   workspace: caller-owned device memory of at least
+ *   fa_backward_workspace_bytes(B,H,Nq) bytes (holds D); contents on entry
+ *   ignored, left undefined. Calls that overlap in time must not share it.
+ *   scale, causal, D, sizes and alignment as fa_forward. dQ, dK, dV must not
+ *   overlap each other, any input or the workspace.
+ *   B*H == 0, or Nq == Nk == 0: nothing to do, FA_OK. Nq == 0 < Nk: no query
+ *   reads a key, so dK and dV are set to zero and only K, V, dK, dV are
+ *   looked at. Nk == 0 < Nq: FA_ERR_INVALID_ARG (the forward pass is
+ *   undefined there).
+ * Products use bf16 MFMA with fp32 accumulation; P and dS are rounded to bf16
+ * before the products that consume them. Three kernels run on `stream`: the
+ * row dot products D, then dQ, then dK and dV.
+ */
+fa_status fa_backward(const void* Q, const void* K, const void* V,
+                      const void* O, const void* dO, const float* LSE,
+                      void* dQ, void* dK, void* dV,
+                      void* workspace, size_t workspace_bytes,
+                      int B, int H, int Nq, int Nk, int D,
+                      float scale, int causal, hipStream_t stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa_status_string(fa_status s);

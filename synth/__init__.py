@@ -7,7 +7,8 @@ Both the HIP path and the oracle receive exactly the tensors produced here;
 the oracle widens the same bf16/fp32 values to fp64.
 
 Recipe: each tensor has its own ``torch.Generator`` seeded with
-``seed * 1_000_003 + tensor_id`` (Q = 0, K = 1, V = 2) on the device the tensor
+``seed * 1_000_003 + tensor_id`` (Q = 0, K = 1, V = 2, the
+output gradient dO = 3) on the device the tensor
 will live on. Values are drawn in fp32, multiplied in fp32 by the workload's
 factor (3 for Q and K of the rescale-stress workload), then rounded to the
 storage dtype by torch's round-to-nearest-even cast. Large tensors are drawn in
@@ -22,7 +23,7 @@ import math
 
 import torch
 
-Q_ID, K_ID, V_ID = 0, 1, 2
+Q_ID, K_ID, V_ID, DO_ID = 0, 1, 2, 3
 
 
 @dataclasses.dataclass(frozen=True)
@@ -93,3 +94,8 @@ def make_qkv(B, H, Nq, Nk, D, dtype, seed: int = 0, device="cpu", qk_mul: float 
 
 def make_workload(w: Workload, seed: int = 0, device="cpu"):
     return make_qkv(w.B, w.H, w.Nq, w.Nk, w.D, w.dtype, seed, device, w.qk_mul)
+
+
+def make_do(B, H, Nq, D, dtype, seed: int = 0, device="cpu"):
+    """Output gradient dO [B,H,Nq,D] ~ N(0, 1) for the backward pass."""
+    return normal((B, H, Nq, D), dtype, seed, DO_ID, device)

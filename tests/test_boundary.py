@@ -34,7 +34,8 @@ def declared_functions():
 
 def test_header_declares_the_api():
     assert declared_functions() == sorted(
-        ["fa_forward", "fa_forward_f32", "fa_decode_workspace_bytes", "fa_decode_splitkv", "fa_status_string"])
+        ["fa_forward", "fa_forward_f32", "fa_decode_workspace_bytes", "fa_decode_splitkv",
+         "fa_backward_workspace_bytes", "fa_backward", "fa_status_string"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -112,6 +113,44 @@ def test_decode_rejects_bad_arguments(lib):
     assert dec(lib, B=0, Q=None, K=None, V=None, O=None, W=None) == 0
 
 
+def test_backward_workspace_bytes(lib):
+    assert lib.fa_backward_workspace_bytes(2, 3, 100) == 2 * 3 * 100 * 4
+    assert lib.fa_backward_workspace_bytes(1, 32, 2048) == 32 * 2048 * 4
+    assert lib.fa_backward_workspace_bytes(-1, 1, 4) == 0
+
+
+def bwd(lib, Q=FAKE, K=FAKE + 0x100000, V=FAKE + 0x200000, O=FAKE + 0x300000, dO=FAKE + 0x400000,
+        L=FAKE + 0x500000, dQ=FAKE + 0x600000, dK=FAKE + 0x700000, dV=FAKE + 0x800000, W=FAKE + 0x900000,
+        wbytes=None, B=2, H=2, Nq=100, Nk=100, D=128, scale=0.1, causal=0):
+    if wbytes is None:
+        wbytes = max(B * H * Nq * 4, 0)
+    return lib.fa_backward(Q, K, V, O, dO, L, dQ, dK, dV, W, wbytes, B, H, Nq, Nk, D, scale, causal, None)
+
+
+def test_backward_rejects_bad_arguments(lib):
+    for name in ("Q", "K", "V", "O", "dO", "L", "dQ", "dK", "dV", "W"):
+        assert bwd(lib, **{name: None}) == INVALID, name
+    assert bwd(lib, dO=FAKE + 0x400008) == INVALID                   # misaligned
+    assert bwd(lib, L=FAKE + 0x500002) == INVALID                    # misaligned LSE
+    assert bwd(lib, wbytes=2 * 2 * 100 * 4 - 4) == INVALID           # workspace one float short
+    assert bwd(lib, Nk=0) == INVALID
+    assert bwd(lib, Nq=-1) == INVALID
+    assert bwd(lib, scale=float("nan")) == INVALID
+    assert bwd(lib, D=96) == UNSUPPORTED
+    assert bwd(lib, dQ=FAKE) == INVALID                              # dQ aliases Q
+    assert bwd(lib, dK=FAKE + 0x500000) == INVALID                   # dK overlaps LSE
+    assert bwd(lib, dV=FAKE + 0x700000 + 64) == INVALID              # dV overlaps dK
+    assert bwd(lib, W=FAKE + 0x600000) == INVALID                    # workspace overlaps dQ
+    assert bwd(lib, B=65536, H=65536, Nq=1024) == UNSUPPORTED        # grid too large
+    # nothing to compute: returns before any pointer is looked at
+    none = dict(Q=None, K=None, V=None, O=None, dO=None, L=None, dQ=None, dK=None, dV=None, W=None)
+    assert bwd(lib, B=0, **none) == 0
+    assert bwd(lib, Nq=0, Nk=0, **none) == 0
+    # Nq = 0 < Nk zeroes dK, dV: those two must be valid
+    assert bwd(lib, Nq=0, dK=None) == INVALID
+    assert bwd(lib, Nq=0, dV=FAKE + 0x700000) == INVALID             # dV aliases dK
+
+
 def test_python_binding_refuses_cpu_tensors(lib):
     import torch
 
@@ -122,6 +161,8 @@ def test_python_binding_refuses_cpu_tensors(lib):
         fa.fa_forward(q, q, q)
     with pytest.raises(ValueError, match="ROCm GPU"):
         fa.fa_decode_splitkv(q[:, :, :1], q, q, num_splits=2)
+    with pytest.raises(ValueError, match="ROCm GPU"):
+        fa.fa_backward(q, q, q, q, q, torch.zeros(1, 1, 4))
 
 
 def test_product_path_does_not_import_the_oracle():
