@@ -4,7 +4,9 @@ One step = one ``fa_forward`` call over the prefill workload the metric is
 quoted on (B=1, H=32, Nq=Nk=2048, D=128, bf16, non-causal), inputs already
 resident in HBM. The metric's second half, split-KV decode bandwidth, is
 measured in the same run on the decode workload (B=16, H=32, one query,
-Nk=32768, D=128, 64 splits) and reported under "decode". Prints ONE JSON line.
+Nk=32768, D=128, 64 splits) and reported under "decode". The backward pass
+(recompute from the saved LSE) is timed on the prefill workload and reported
+under "backward". Prints ONE JSON line.
 
 Timing: W untimed warm-up steps plus untimed steps until half a second of GPU
 work has run (the engine clock ramps up under load), then K steps between two
@@ -15,6 +17,8 @@ sides.
 Algorithmic counts (not the implementation's):
   prefill FLOPs = 4*B*H*Nq*Nk*D (halved when causal)
   bytes         = Q, K, V read once + O written once (+ LSE, fp32)
+  backward FLOPs = 10*B*H*Nq*Nk*D (S, dP, dV, dQ, dK: five products; halved
+                   when causal), the recompute of S counted
 """
 
 from __future__ import annotations
@@ -139,6 +143,9 @@ def main():
     ap.add_argument("--decode-workload", default="decode_b16_h32_kv32768_d128_s64")
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--backward-workload", default=None, help="default: --workload")
+    ap.add_argument("--backward-steps", type=int, default=50)
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -231,6 +238,32 @@ def main():
                          "kernel_source_digest": ddigest},
         }
         del dq, dk, dv, ws
+
+    if not args.no_backward:
+        bw = synth.WORKLOADS[args.backward_workload or args.workload]
+        if bw.dtype != torch.bfloat16 or bw.is_decode:
+            raise SystemExit("the backward pass is bf16 prefill only")
+        bq, bk, bv = synth.make_workload(bw, seed=0, device="cuda")
+        bdo = synth.make_do(bw.B, bw.H, bw.Nq, bw.D, bw.dtype, seed=0, device="cuda")
+        bo, blse = fa.fa_forward(bq, bk, bv, causal=bw.causal, scale=bw.scale)
+        grads = tuple(torch.empty_like(t) for t in (bq, bk, bv))
+        bws = torch.empty(max(16, fa.fa_backward_workspace_bytes(bw.B, bw.H, bw.Nq)), dtype=torch.uint8,
+                          device="cuda")
+        bstep = lambda: fa.fa_backward(bq, bk, bv, bo, bdo, blse, causal=bw.causal, scale=bw.scale,  # noqa: E731
+                                       workspace=bws, dq=grads[0], dk=grads[1], dv=grads[2])
+        bms = time_steps(bstep, args.backward_steps, args.warmup, torch)
+        fwd_flops, _ = workload_counts(bw)
+        btf = 2.5 * fwd_flops / (bms * 1e-3) / 1e12
+        result["backward"] = {
+            "workload": bw.name, "ms_per_call": round(bms, 6), "value": round(btf, 3), "unit": "TFLOP/s",
+            "algorithmic_flops": 2.5 * fwd_flops,
+            "roofline": {"kernel": "bwd_rowdot_kernel + bwd_dq_kernel + bwd_dkdv_kernel", "bound": "mfma",
+                         "achieved": round(btf, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(btf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                         "kernel_source_digest": kernel_source_digest(["fa_bwd.hip", "fa_device.h",
+                                                                       "fa_internal.h"])},
+        }
+        del bq, bk, bv, bdo, bo, grads, bws
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
