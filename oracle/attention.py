@@ -61,49 +61,84 @@ def _f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def allowed_keys(i: int, nk: int, causal: bool) -> np.ndarray:
+CAUSAL_NONE, CAUSAL_TOP_LEFT, CAUSAL_BOTTOM_RIGHT = 0, 1, 2
+
+
+def allowed_keys(i: int, nk: int, causal, nq: int | None = None, kv_len: int | None = None) -> np.ndarray:
     """Boolean mask of the keys query row ``i`` may attend.
 
-    Keys are 0..nk-1. With ``causal`` the row attends only keys j <= i,
-    counted from the first key (top-left alignment: the exercise "Causal mask"
-    defines it on square inputs, and the same absolute rule is kept when
-    Nq != Nk).
+    Keys are 0..nk-1, of which the first ``kv_len`` (default all) are real and
+    the rest padding, never attended (the padding masks of the Pitfalls
+    passage). ``causal``:
+
+    * False / 0: every real key;
+    * True / 1, top-left: keys j <= i, counted from the first key (the
+      exercise "Causal mask" defines it on square inputs; the same absolute
+      rule is kept when Nq != Nk);
+    * 2, bottom-right: the last of the ``nq`` query rows is aligned with the
+      last real key, j <= i + (kv_len - nq). This is the reading for Nq != Nk
+      in which the queries are the newest tokens of the sequence; it equals
+      top-left when kv_len == nq, and rows i < nq - kv_len see no key at all.
+
+    A row may end up with no allowed key (padding, bottom-right): see
+    ``attention_rows`` for its value.
     """
     j = np.arange(nk)
-    if causal:
-        return j <= i
-    return np.ones(nk, dtype=bool)
+    real = j < (nk if kv_len is None else kv_len)
+    mode = int(causal)
+    if mode == CAUSAL_TOP_LEFT:
+        return real & causal_top_left(i, j)
+    if mode == CAUSAL_BOTTOM_RIGHT:
+        off = (nk if kv_len is None else kv_len) - nq
+        return real & (j <= i + off)
+    return real
 
 
-def attention_rows(q_rows, row_index, k, v, scale: float, causal: bool):
+def causal_top_left(i, j):
+    return j <= i
+
+
+def attention_rows(q_rows, row_index, k, v, scale: float, causal, nq: int | None = None,
+                   kv_len: int | None = None):
     """Two-pass attention for selected query rows of one (batch, head).
 
     q_rows: [R, D] queries; row_index: [R] their absolute row numbers (used by
-    the causal mask); k, v: [Nk, D]. Returns (O [R, D], LSE [R]).
+    the causal mask); k, v: [Nk, D]; nq: the number of query rows of the head
+    (bottom-right alignment); kv_len: real keys (default Nk). Returns
+    (O [R, D], LSE [R]).
 
     Follows section 11.2 and the stable softmax of the iThome article: the
     score row s = scale * q . k_j is materialised, m = max over the allowed
     keys, p = exp(s - m), l = sum p, O = (sum_j p_j v_j) / l. LSE = m + ln l
     on the scaled scores, as the write-back step of the FA2 visualization
     stores it.
+
+    A row with no allowed key (the fully masked row of the Pitfalls passage)
+    has no softmax; it gets the values of the empty sums the definition
+    reduces to: O = 0 (no value vector is weighted) and LSE = ln 0 = -inf.
     """
     q_rows, k, v = _f64(q_rows), _f64(k), _f64(v)
     nk = k.shape[0]
     s = scale * (q_rows @ k.T)                       # [R, Nk]
-    mask = np.stack([allowed_keys(int(i), nk, causal) for i in row_index])
+    mask = np.stack([allowed_keys(int(i), nk, causal, nq, kv_len) for i in row_index]).reshape(s.shape)
+    empty = ~mask.any(axis=1)
     s = np.where(mask, s, NEG_INF)
     m = s.max(axis=1, keepdims=True)
+    m[empty] = 0.0                                    # no key: keep exp(-inf - 0) = 0
     p = np.exp(s - m)                                 # exp(-inf) = 0 for masked keys
     l = p.sum(axis=1, keepdims=True)
-    o = (p @ v) / l
-    lse = m[:, 0] + np.log(l[:, 0])
+    l_div = np.where(empty[:, None], 1.0, l)
+    o = (p @ v) / l_div
+    with np.errstate(divide="ignore"):
+        lse = m[:, 0] + np.log(l[:, 0])               # ln 0 = -inf on empty rows
     return o, lse
 
 
-def attention(q, k, v, scale: float, causal: bool = False):
+def attention(q, k, v, scale: float, causal=False, kv_lens=None):
     """softmax(Q K^T * scale) V over tensors laid out [B, H, N, D].
 
-    q: [B, H, Nq, D]; k, v: [B, H, Nk, D]. Returns O [B, H, Nq, D] and
+    q: [B, H, Nq, D]; k, v: [B, H, Nk, D]; kv_lens: optional [B] real key
+    counts (keys past them are padding). Returns O [B, H, Nq, D] and
     LSE [B, H, Nq] in float64. This is the definition the method reaches
     exactly (the iThome article calls FlashAttention exact attention): every
     row is computed in two passes by ``attention_rows``.
@@ -114,24 +149,30 @@ def attention(q, k, v, scale: float, causal: bool = False):
     lse = np.empty((b, h, nq))
     rows = np.arange(nq)
     for bi in range(b):
+        kv_len = None if kv_lens is None else int(kv_lens[bi])
         for hi in range(h):
-            o[bi, hi], lse[bi, hi] = attention_rows(q[bi, hi], rows, k[bi, hi], v[bi, hi], scale, causal)
+            o[bi, hi], lse[bi, hi] = attention_rows(q[bi, hi], rows, k[bi, hi], v[bi, hi], scale, causal,
+                                                    nq, kv_len)
     return o, lse
 
 
-def softmax_weights(q, k, scale: float, causal: bool = False):
+def softmax_weights(q, k, scale: float, causal=False, kv_len: int | None = None):
     """The probability matrix P = softmax(scale * Q K^T) of one (batch, head).
 
-    q: [Nq, D], k: [Nk, D] -> P [Nq, Nk]; masked entries are exactly 0.
-    Exposed so tests can check that every row sums to one.
+    q: [Nq, D], k: [Nk, D] -> P [Nq, Nk]; masked entries are exactly 0, and
+    so is every entry of a row with no allowed key. Exposed so tests can check
+    that every (non-empty) row sums to one.
     """
     q, k = _f64(q), _f64(k)
-    nk = k.shape[0]
+    nq, nk = q.shape[0], k.shape[0]
     s = scale * (q @ k.T)
-    mask = np.stack([allowed_keys(i, nk, causal) for i in range(q.shape[0])])
+    mask = np.stack([allowed_keys(i, nk, causal, nq, kv_len) for i in range(nq)]).reshape(s.shape)
+    empty = ~mask.any(axis=1)
     s = np.where(mask, s, NEG_INF)
-    p = np.exp(s - s.max(axis=1, keepdims=True))
-    return p / p.sum(axis=1, keepdims=True)
+    m = s.max(axis=1, keepdims=True)
+    m[empty] = 0.0
+    p = np.exp(s - m)
+    return p / np.where(empty[:, None], 1.0, p.sum(axis=1, keepdims=True))
 
 
 # --------------------------------------------------------------------------
@@ -170,7 +211,7 @@ def online_per_key(s, v, trace: bool = False):
     return m, l, o
 
 
-def online_blocked(q, k, v, scale: float, causal: bool, block: int):
+def online_blocked(q, k, v, scale: float, causal, block: int, kv_len: int | None = None):
     """Block-wise online softmax over keys (the FA2 form of the iThome article).
 
     For each query row of one (batch, head) and each block of ``block`` keys:
@@ -178,15 +219,16 @@ def online_blocked(q, k, v, scale: float, causal: bool, block: int):
     alpha = exp(m - m_new), P = exp(S_blk - m_new), l = alpha l + sum P,
     O = alpha O + P V_blk, m = m_new; after the last block O / l and
     LSE = m + ln l. A block may hold fewer than ``block`` keys at the end
-    (the masked last block of the phobos ``attention``). Plain loops: tiny
-    inputs only.
+    (the masked last block of the phobos ``attention``). A row that never sees
+    an allowed key ends with l = 0 and gets O = 0, LSE = -inf. Plain loops:
+    tiny inputs only.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     nq, nk = q.shape[0], k.shape[0]
     out = np.zeros((nq, v.shape[1]))
     lse = np.zeros(nq)
     for i in range(nq):
-        ok = allowed_keys(i, nk, causal)
+        ok = allowed_keys(i, nk, causal, nq, kv_len)
         m, l = NEG_INF, 0.0
         acc = np.zeros(v.shape[1])
         for j0 in range(0, nk, block):
@@ -201,6 +243,9 @@ def online_blocked(q, k, v, scale: float, causal: bool, block: int):
             l = alpha * l + p.sum()
             acc = alpha * acc + p @ v[j0:j1]
             m = m_new
+        if l == 0.0:                      # no allowed key (see attention_rows)
+            out[i], lse[i] = 0.0, NEG_INF
+            continue
         out[i] = acc / l
         lse[i] = m + math.log(l)
     return out, lse
@@ -248,19 +293,23 @@ def split_states(q_row, k, v, scale: float, num_splits: int):
 
 
 def combine(parts):
-    """Fold a list of partial states with ``merge`` and finish: (o / l, m + ln l)."""
+    """Fold a list of partial states with ``merge`` and finish: (o / l, m + ln l),
+    or (0, -inf) when no chunk held a key."""
     state = (NEG_INF, 0.0, np.zeros_like(_f64(parts[0][2])))
     for p in parts:
         state = merge(state, p)
     m, l, o = state
+    if l == 0.0:                          # every chunk empty: no key at all
+        return np.zeros_like(o), NEG_INF
     return o / l, m + math.log(l)
 
 
-def decode(q, k, v, scale: float):
-    """Single-token decode: q [B, H, 1, D] over the whole cache k, v [B, H, Nk, D],
-    no mask. The same definition as ``attention`` with Nq = 1; returns
-    O [B, H, 1, D] and LSE [B, H, 1]."""
-    return attention(q, k, v, scale, causal=False)
+def decode(q, k, v, scale: float, kv_lens=None):
+    """Single-token decode: q [B, H, 1, D] over the cache k, v [B, H, Nk, D],
+    of which the first kv_lens[b] keys (default all) are real. No causal mask.
+    The same definition as ``attention`` with Nq = 1; returns O [B, H, 1, D]
+    and LSE [B, H, 1]."""
+    return attention(q, k, v, scale, causal=False, kv_lens=kv_lens)
 
 
 # --------------------------------------------------------------------------
@@ -268,7 +317,7 @@ def decode(q, k, v, scale: float):
 # dV from O, dO and the saved log-sum-exp).
 # --------------------------------------------------------------------------
 
-def attention_backward_head(q, k, v, do, scale: float, causal: bool = False):
+def attention_backward_head(q, k, v, do, scale: float, causal=False, kv_len: int | None = None):
     """Gradients of O = softmax(scale * Q K^T) V for one (batch, head).
 
     q: [Nq, D], k, v: [Nk, D], do: [Nq, D] (the gradient of the loss with
@@ -282,10 +331,11 @@ def attention_backward_head(q, k, v, do, scale: float, causal: bool = False):
         dS = P * (dP - rowsum(P * dP))      (softmax Jacobian, row by row)
         dQ = scale * dS K,   dK = scale * dS^T Q
     rowsum(P * dP) equals rowsum(dO * O) because O = P V; the kernels use the
-    second form, this definition the first.
+    second form, this definition the first. A row with no allowed key has
+    P = 0 (its O = 0 does not depend on Q, K or V), so it adds nothing.
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
-    p = softmax_weights(q, k, scale, causal)         # [Nq, Nk]
+    p = softmax_weights(q, k, scale, causal, kv_len)  # [Nq, Nk]
     dv = p.T @ do
     dp = do @ v.T
     ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
@@ -294,7 +344,7 @@ def attention_backward_head(q, k, v, do, scale: float, causal: bool = False):
     return dq, dk, dv
 
 
-def attention_backward(q, k, v, do, scale: float, causal: bool = False):
+def attention_backward(q, k, v, do, scale: float, causal=False, kv_lens=None):
     """``attention_backward_head`` over [B, H, N, D] tensors; returns
     (dQ, dK, dV) in float64 with the shapes of q, k, v."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
@@ -302,7 +352,8 @@ def attention_backward(q, k, v, do, scale: float, causal: bool = False):
     dk = np.empty_like(k)
     dv = np.empty_like(v)
     for bi in range(q.shape[0]):
+        kv_len = None if kv_lens is None else int(kv_lens[bi])
         for hi in range(q.shape[1]):
             dq[bi, hi], dk[bi, hi], dv[bi, hi] = attention_backward_head(
-                q[bi, hi], k[bi, hi], v[bi, hi], do[bi, hi], scale, causal)
+                q[bi, hi], k[bi, hi], v[bi, hi], do[bi, hi], scale, causal, kv_len)
     return dq, dk, dv

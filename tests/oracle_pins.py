@@ -315,6 +315,198 @@ def pin_backward_closed_forms(orc):
             _close(dq[0, 0, 0], np.zeros(4), 0.0, "causal row 0 dQ")
 
 
+# ---- padding masks, bottom-right alignment, fully masked rows ------------------
+
+def _allowed_count(i, nq, nk, causal, kv_len):
+    """How many keys row i may attend, counted by hand from the rule."""
+    L = nk if kv_len is None else kv_len
+    if causal == 0:
+        return L
+    last = i if causal == 1 else i + (L - nq)      # last visible key index
+    return max(0, min(L, last + 1))
+
+
+def pin_mask_closed_forms(orc):
+    """K = 0: each allowed key weighs 1/count, so O is the mean of the first
+    count V rows and LSE = ln(count); a row with no allowed key has O = 0 and
+    LSE = -inf (the empty sums). Padding, top-left and bottom-right, Nq < Nk,
+    Nq > Nk, and a batch entry with no real key."""
+    for (nq, nk, causal, kv_lens) in [(6, 9, 0, [9, 4]), (6, 9, 1, [7, 0]), (6, 9, 2, [9, 5]),
+                                      (9, 5, 2, [5, 3]), (9, 5, 1, [2, 5]), (4, 4, 2, [4, 1])]:
+        q = _rand((2, 2, nq, 3), nq * 7 + nk)
+        k = np.zeros((2, 2, nk, 3))
+        v = _rand((2, 2, nk, 3), nq * 11 + nk)
+        o, lse = orc.attention(q, k, v, 0.7, causal, kv_lens=kv_lens)
+        for b in range(2):
+            for i in range(nq):
+                c = _allowed_count(i, nq, nk, causal, kv_lens[b])
+                tag = f"K=0 nq={nq} nk={nk} causal={causal} len={kv_lens[b]} row {i}"
+                if c == 0:
+                    _close(o[b, :, i], np.zeros((2, 3)), 0.0, tag + " O")
+                    assert np.all(lse[b, :, i] == -math.inf), tag + " LSE"
+                else:
+                    _close(o[b, :, i], v[b, :, :c].mean(axis=1), 1e-14, tag + " O")
+                    _close(lse[b, :, i], np.full(2, math.log(c)), 1e-14, tag + " LSE")
+
+
+def pin_padding_is_truncation(orc):
+    """Keys past kv_len are invisible: the result equals attention over the
+    first kv_len keys alone, whatever the padded keys hold."""
+    nq, nk, L = 7, 12, 8
+    q = _rand((1, 2, nq, 4), 60) * 2.0
+    k = _rand((1, 2, nk, 4), 61) * 2.0
+    v = _rand((1, 2, nk, 4), 62)
+    for causal in (0, 1, 2):
+        o, lse = orc.attention(q, k, v, 0.5, causal, kv_lens=[L])
+        o_t, lse_t = orc.attention(q, k[:, :, :L], v[:, :, :L], 0.5, causal)
+        _close(o, o_t, 1e-14, f"padding = truncation O causal={causal}")
+        _close(lse, lse_t, 1e-14, f"padding = truncation LSE causal={causal}")
+        k2, v2 = k.copy(), v.copy()
+        k2[:, :, L:] = 1e3
+        v2[:, :, L:] = -7.0
+        o2, lse2 = orc.attention(q, k2, v2, 0.5, causal, kv_lens=[L])
+        _close(o2, o, 0.0, f"padded keys ignored causal={causal}")
+        _close(lse2, lse, 0.0, f"padded keys ignored LSE causal={causal}")
+
+
+def pin_bottom_right_is_suffix(orc):
+    """Bottom-right causal on Nq queries equals the last Nq rows of top-left
+    causal attention over Nk queries whose last rows are those queries
+    (Nq <= Nk); with Nq > Nk the first Nq - Nk rows see no key and the rest
+    are square top-left causal attention of the last Nk queries."""
+    nk, d = 11, 4
+    k = _rand((1, 1, nk, d), 63) * 2.0
+    v = _rand((1, 1, nk, d), 64)
+    for nq in (1, 4, 11):
+        full_q = _rand((1, 1, nk, d), 65 + nq) * 2.0
+        q = full_q[:, :, nk - nq:]
+        o, lse = orc.attention(q, k, v, 0.5, 2)
+        o_f, lse_f = orc.attention(full_q, k, v, 0.5, True)
+        _close(o, o_f[:, :, nk - nq:], 1e-14, f"bottom-right nq={nq} O")
+        _close(lse, lse_f[:, :, nk - nq:], 1e-14, f"bottom-right nq={nq} LSE")
+    nq = 15
+    q = _rand((1, 1, nq, d), 66) * 2.0
+    o, lse = orc.attention(q, k, v, 0.5, 2)
+    o_sq, lse_sq = orc.attention(q[:, :, nq - nk:], k, v, 0.5, True)
+    _close(o[:, :, nq - nk:], o_sq, 1e-14, "bottom-right nq>nk tail O")
+    _close(lse[:, :, nq - nk:], lse_sq, 1e-14, "bottom-right nq>nk tail LSE")
+    _close(o[:, :, : nq - nk], np.zeros((1, 1, nq - nk, d)), 0.0, "bottom-right empty rows O")
+    assert np.all(lse[:, :, : nq - nk] == -math.inf), "bottom-right empty rows LSE"
+
+
+def pin_masks_torch_sdpa(orc):
+    """torch's float64 CPU scaled_dot_product_attention with an explicit
+    boolean mask (an independent library routine) on every row that has an
+    allowed key, for padding and both causal alignments."""
+    for (nq, nk, causal, kv_lens, seed) in [(9, 14, 2, [14, 10], 70), (12, 6, 2, [6, 4], 71),
+                                            (8, 13, 1, [5, 13], 72), (10, 10, 0, [3, 10], 73)]:
+        q = _rand((2, 2, nq, 8), seed) * 2.0
+        k = _rand((2, 2, nk, 8), seed + 1) * 2.0
+        v = _rand((2, 2, nk, 8), seed + 2)
+        o, lse = orc.attention(q, k, v, 0.3, causal, kv_lens=kv_lens)
+        i = torch.arange(nq)[:, None]
+        j = torch.arange(nk)[None, :]
+        for b in range(2):
+            L = kv_lens[b]
+            mask = (j < L) & torch.ones(nq, nk, dtype=torch.bool)
+            if causal == 1:
+                mask = mask & (j <= i)
+            elif causal == 2:
+                mask = mask & (j <= i + (L - nq))
+            rows = mask.any(dim=1)
+            tq, tk, tv = (torch.from_numpy(x[b]) for x in (q, k, v))
+            ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=0.3)
+            s = (0.3 * (tq @ tk.transpose(-1, -2))).masked_fill(~mask, -math.inf)
+            tag = f"sdpa mask nq={nq} nk={nk} causal={causal} len={L}"
+            _close(o[b][:, rows.numpy()], ref.numpy()[:, rows.numpy()], 1e-12, tag)
+            _close(lse[b][:, rows.numpy()], torch.logsumexp(s, dim=-1).numpy()[:, rows.numpy()], 1e-12, tag)
+
+
+def pin_online_blocked_masks(orc):
+    """The block-wise online recurrence reaches the two-pass result under
+    padding and bottom-right masks, empty rows included."""
+    for (nq, nk, causal, L) in [(7, 10, 2, 10), (12, 6, 2, 4), (6, 9, 1, 0), (5, 9, 0, 6)]:
+        q = _rand((nq, 5), 80 + nq) * 3.0
+        k = _rand((nk, 5), 81 + nk) * 3.0
+        v = _rand((nk, 5), 82 + nq)
+        o_ref, l_ref = orc.attention(q[None, None], k[None, None], v[None, None], 0.45, causal, kv_lens=[L])
+        for block in (1, 3, 4, nk + 2):
+            o, l = orc.online_blocked(q, k, v, 0.45, causal, block, kv_len=L)
+            _close(o, o_ref[0, 0], 1e-12, f"blocked masked O block={block}")
+            assert np.array_equal(np.isinf(l), np.isinf(l_ref[0, 0])), "blocked masked empty rows"
+            fin = np.isfinite(l)
+            _close(l[fin], l_ref[0, 0][fin], 1e-12, f"blocked masked LSE block={block}")
+
+
+def pin_decode_padding(orc):
+    """Decode over a padded cache = the chunked merge over the real keys only;
+    a cache with no real key gives (0, -inf)."""
+    nk = 40
+    q = _rand((2, 1, 1, 6), 90) * 2.0
+    k = _rand((2, 1, nk, 6), 91) * 2.0
+    v = _rand((2, 1, nk, 6), 92)
+    o, lse = orc.decode(q, k, v, 0.4, kv_lens=[23, 0])
+    for splits in (1, 4, 64):
+        parts = orc.split_states(q[0, 0, 0], k[0, 0, :23], v[0, 0, :23], 0.4, splits)
+        o_c, l_c = orc.combine(parts)
+        _close(o[0, 0, 0], o_c, 1e-13, f"padded decode S={splits}")
+        _close(lse[0, 0, 0], l_c, 1e-13, f"padded decode LSE S={splits}")
+    o_e, l_e = orc.combine([(-math.inf, 0.0, np.zeros(6))] * 3)
+    _close(o_e, np.zeros(6), 0.0, "all-empty combine O")
+    assert l_e == -math.inf
+    _close(o[1, 0, 0], np.zeros(6), 0.0, "decode with no real key O")
+    assert lse[1, 0, 0] == -math.inf
+
+
+def pin_backward_masks(orc):
+    """Backward under padding and bottom-right masks: central differences of
+    the forward oracle, torch fp64 autograd with an explicit mask (rows with
+    keys only: torch's gradient through an empty row is NaN), padded keys
+    get dK = dV = 0 and empty rows dQ = 0."""
+    h = 1e-6
+    for (nq, nk, causal, L, seed) in [(5, 4, 2, 4, 93), (3, 6, 2, 5, 94), (4, 5, 1, 3, 95)]:
+        q = _rand((1, 1, nq, 2), seed) * 1.5
+        k = _rand((1, 1, nk, 2), seed + 1) * 1.5
+        v = _rand((1, 1, nk, 2), seed + 2)
+        g = _rand((1, 1, nq, 2), seed + 3)
+        dq, dk, dv = orc.attention_backward(q, k, v, g, 0.6, causal, kv_lens=[L])
+
+        def loss(qq, kk, vv):
+            return float(np.sum(orc.attention(qq, kk, vv, 0.6, causal, kv_lens=[L])[0] * g))
+
+        for pos, (name, grad) in enumerate((("Q", dq), ("K", dk), ("V", dv))):
+            x = (q, k, v)[pos]
+            num = np.zeros_like(x)
+            for idx in np.ndindex(*x.shape):
+                args_p, args_m = [q, k, v], [q, k, v]
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                args_p[pos], args_m[pos] = xp, xm
+                num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            _close(grad, num, 1e-7, f"masked finite differences d{name} nq={nq} nk={nk} causal={causal}")
+        _close(dk[:, :, L:], np.zeros_like(dk[:, :, L:]), 0.0, "padded keys dK")
+        _close(dv[:, :, L:], np.zeros_like(dv[:, :, L:]), 0.0, "padded keys dV")
+    nq, nk, L = 9, 7, 5
+    q = _rand((1, 2, nq, 4), 96) * 2.0
+    k = _rand((1, 2, nk, 4), 97) * 2.0
+    v = _rand((1, 2, nk, 4), 98)
+    g = _rand((1, 2, nq, 4), 99)
+    dq, dk, dv = orc.attention_backward(q, k, v, g, 0.5, 2, kv_lens=[L])
+    i = torch.arange(nq)[:, None]
+    j = torch.arange(nk)[None, :]
+    mask = (j < L) & (j <= i + (L - nq))
+    rows = mask.any(dim=1)
+    assert not rows[: nq - L].any() and rows[nq - L:].all()
+    _close(dq[0, :, : nq - L], np.zeros((2, nq - L, 4)), 0.0, "empty rows dQ")
+    tq, tk, tv = (torch.from_numpy(x[0]).requires_grad_(True) for x in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq[:, rows], tk, tv, attn_mask=mask[rows], scale=0.5)
+    out.backward(torch.from_numpy(g[0][:, rows.numpy()]))
+    _close(dq[0][:, rows.numpy()], tq.grad.numpy()[:, rows.numpy()], 1e-12, "masked autograd dQ")
+    _close(dk[0], tk.grad.numpy(), 1e-12, "masked autograd dK")
+    _close(dv[0], tv.grad.numpy(), 1e-12, "masked autograd dV")
+
+
 ALL_PINS = [
     pin_worked_example_trace,
     pin_worked_example_two_pass,
@@ -333,4 +525,11 @@ ALL_PINS = [
     pin_backward_finite_differences,
     pin_backward_torch_autograd,
     pin_backward_closed_forms,
+    pin_mask_closed_forms,
+    pin_padding_is_truncation,
+    pin_bottom_right_is_suffix,
+    pin_masks_torch_sdpa,
+    pin_online_blocked_masks,
+    pin_decode_padding,
+    pin_backward_masks,
 ]

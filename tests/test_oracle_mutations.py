@@ -15,8 +15,18 @@ MUTATIONS = {
     "dropped_scale": ("s = scale * (q_rows @ k.T)", "s = (q_rows @ k.T)"),
     "lse_without_max": ("lse = m[:, 0] + np.log(l[:, 0])", "lse = np.log(l[:, 0])"),
     "lse_base_two": ("lse = m[:, 0] + np.log(l[:, 0])", "lse = m[:, 0] + np.log2(l[:, 0])"),
-    "no_final_divide": ("o = (p @ v) / l", "o = (p @ v)"),
-    "wrong_operand": ("o = (p @ v) / l", "o = (p @ k) / l"),
+    "no_final_divide": ("o = (p @ v) / l_div", "o = (p @ v)"),
+    "wrong_operand": ("o = (p @ v) / l_div", "o = (p @ k) / l_div"),
+    "bottom_right_off_by_one": ("return real & (j <= i + off)", "return real & (j < i + off)"),
+    "bottom_right_wrong_length": ("off = (nk if kv_len is None else kv_len) - nq", "off = nk - nq"),
+    "padding_includes_boundary": ("real = j < (nk if kv_len is None else kv_len)",
+                                  "real = j <= (nk if kv_len is None else kv_len)"),
+    "padding_ignored_in_backward": ("p = softmax_weights(q, k, scale, causal, kv_len)",
+                                    "p = softmax_weights(q, k, scale, causal)"),
+    "empty_row_lse_zero": ("lse = m[:, 0] + np.log(l[:, 0])               # ln 0",
+                           "lse = m[:, 0] + np.log(np.maximum(l[:, 0], 1.0))  # ln 0"),
+    "empty_combine_nan": ("    if l == 0.0:                          # every chunk empty: no key at all",
+                          "    if False:"),
     "unshifted_exp": ("p = np.exp(s - m)                                 #", "p = np.exp(s)                                     #"),
     "per_key_forgot_rescale": ("o = o * corr + p * v[j]", "o = o + p * v[j]"),
     "per_key_l_not_rescaled": ("l = l * corr + p", "l = l + p"),
