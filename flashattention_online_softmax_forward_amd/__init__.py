@@ -6,6 +6,11 @@ torch supplies device memory and the current stream. Tensors are [B, H, N, D]
 contiguous on a ROCm device; outputs are allocated here with torch when the
 caller does not pass them. There is no CPU fallback: without the built library
 or a GPU tensor these functions raise.
+
+``causal`` is False / 0 (no mask), True / 1 / "top_left" (key j <= query i) or
+2 / "bottom_right" (key j <= i + Lk - Nq). ``kv_lens`` (optional int32 [B] on
+the device) gives each batch entry's real key count; keys past it are padding.
+Rows that may attend no key come back as O = 0, LSE = -inf.
 """
 
 from __future__ import annotations
@@ -17,7 +22,12 @@ import torch
 
 from . import _lib
 
+CAUSAL_NONE, CAUSAL_TOP_LEFT, CAUSAL_BOTTOM_RIGHT = 0, 1, 2
+
 __all__ = [
+    "CAUSAL_NONE",
+    "CAUSAL_TOP_LEFT",
+    "CAUSAL_BOTTOM_RIGHT",
     "fa_forward",
     "fa_forward_f32",
     "fa_decode_splitkv",
@@ -52,7 +62,30 @@ def _check_tensor(name: str, t: torch.Tensor, dtype: torch.dtype, ndim: int = 4)
         raise ValueError(f"{name} must be contiguous")
 
 
-def _forward(fn_name, dtype, q, k, v, causal, scale, out, lse, want_lse):
+def _causal_mode(causal) -> int:
+    if isinstance(causal, str):
+        names = {"none": CAUSAL_NONE, "top_left": CAUSAL_TOP_LEFT, "bottom_right": CAUSAL_BOTTOM_RIGHT}
+        if causal not in names:
+            raise ValueError(f"causal must be one of {sorted(names)} (got {causal!r})")
+        return names[causal]
+    mode = int(causal)
+    if mode not in (CAUSAL_NONE, CAUSAL_TOP_LEFT, CAUSAL_BOTTOM_RIGHT):
+        raise ValueError(f"causal must be 0, 1 or 2 (got {causal!r})")
+    return mode
+
+
+def _check_kv_lens(kv_lens, B, device):
+    if kv_lens is None:
+        return None
+    if not isinstance(kv_lens, torch.Tensor) or kv_lens.dtype != torch.int32 or kv_lens.dim() != 1 \
+            or kv_lens.shape[0] != B or not kv_lens.is_contiguous():
+        raise ValueError(f"kv_lens must be a contiguous int32 tensor of shape [{B}]")
+    if kv_lens.device != device:
+        raise ValueError(f"kv_lens must live on {device} (got {kv_lens.device})")
+    return kv_lens
+
+
+def _forward(fn_name, dtype, q, k, v, causal, scale, out, lse, want_lse, kv_lens=None):
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_tensor(name, t, dtype)
     B, H, Nq, D = q.shape
@@ -72,28 +105,37 @@ def _forward(fn_name, dtype, q, k, v, causal, scale, out, lse, want_lse):
         _check_tensor("lse", lse, torch.float32, ndim=3)
         if tuple(lse.shape) != (B, H, Nq):
             raise ValueError("lse must be [B, H, Nq]")
-    fn = getattr(_lib.load(), fn_name)
-    code = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-              lse.data_ptr() if lse is not None else None,
-              B, H, Nq, Nk, D, float(scale), int(bool(causal)), _stream(q))
+    mode = _causal_mode(causal)
+    kv_lens = _check_kv_lens(kv_lens, B, q.device)
+    lib = _lib.load()
+    lse_p = lse.data_ptr() if lse is not None else None
+    if kv_lens is None:
+        code = getattr(lib, fn_name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_p,
+                                     B, H, Nq, Nk, D, float(scale), mode, _stream(q))
+    else:
+        fn_name += "_masked"
+        code = getattr(lib, fn_name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_p,
+                                     kv_lens.data_ptr(), B, H, Nq, Nk, D, float(scale), mode, _stream(q))
     _lib.check(code, fn_name)
     return out, lse
 
 
-def fa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+def fa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal=False,
                scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-               lse: Optional[torch.Tensor] = None, want_lse: bool = True
+               lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+               kv_lens: Optional[torch.Tensor] = None
                ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """bf16 forward: returns (O bf16 [B,H,Nq,D], LSE fp32 [B,H,Nq] or None)."""
-    return _forward("fa_forward", torch.bfloat16, q, k, v, causal, scale, out, lse, want_lse)
+    return _forward("fa_forward", torch.bfloat16, q, k, v, causal, scale, out, lse, want_lse, kv_lens)
 
 
-def fa_forward_f32(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+def fa_forward_f32(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal=False,
                    scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-                   lse: Optional[torch.Tensor] = None, want_lse: bool = True
+                   lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                   kv_lens: Optional[torch.Tensor] = None
                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """fp32 forward: returns (O fp32 [B,H,Nq,D], LSE fp32 [B,H,Nq] or None)."""
-    return _forward("fa_forward_f32", torch.float32, q, k, v, causal, scale, out, lse, want_lse)
+    return _forward("fa_forward_f32", torch.float32, q, k, v, causal, scale, out, lse, want_lse, kv_lens)
 
 
 def fa_decode_workspace_bytes(B: int, H: int, D: int, num_splits: int) -> int:
@@ -103,8 +145,10 @@ def fa_decode_workspace_bytes(B: int, H: int, D: int, num_splits: int) -> int:
 def fa_decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, num_splits: int,
                       scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                      want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Split-KV decode of one query token: q bf16 [B,H,1,D], k/v bf16 [B,H,Nk,D].
+                      want_lse: bool = True, kv_lens: Optional[torch.Tensor] = None
+                      ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Split-KV decode of one query token: q bf16 [B,H,1,D], k/v bf16 [B,H,Nk,D]
+    (of which the first kv_lens[b] keys are real, when given).
     Returns (O bf16 [B,H,1,D], LSE fp32 [B,H] or None). ``workspace`` is a
     device tensor of at least fa_decode_workspace_bytes(B,H,D,num_splits) bytes;
     one is allocated when not given."""
@@ -131,10 +175,16 @@ def fa_decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, num_spl
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
     if lse is not None:
         _check_tensor("lse", lse, torch.float32, ndim=2)
-    code = _lib.load().fa_decode_splitkv(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-        lse.data_ptr() if lse is not None else None, workspace.data_ptr(), ws_bytes,
-        B, H, Nk, D, float(scale), int(num_splits), _stream(q))
+    kv_lens = _check_kv_lens(kv_lens, B, q.device)
+    lse_p = lse.data_ptr() if lse is not None else None
+    if kv_lens is None:
+        code = _lib.load().fa_decode_splitkv(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_p, workspace.data_ptr(), ws_bytes,
+            B, H, Nk, D, float(scale), int(num_splits), _stream(q))
+    else:
+        code = _lib.load().fa_decode_splitkv_masked(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_p, kv_lens.data_ptr(),
+            workspace.data_ptr(), ws_bytes, B, H, Nk, D, float(scale), int(num_splits), _stream(q))
     _lib.check(code, "fa_decode_splitkv")
     return out, lse
 
@@ -144,10 +194,10 @@ def fa_backward_workspace_bytes(B: int, H: int, Nq: int) -> int:
 
 
 def fa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
-                do: torch.Tensor, lse: torch.Tensor, causal: bool = False,
+                do: torch.Tensor, lse: torch.Tensor, causal=False,
                 scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
                 dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
-                dv: Optional[torch.Tensor] = None
+                dv: Optional[torch.Tensor] = None, kv_lens: Optional[torch.Tensor] = None
                 ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """bf16 backward with recompute: q, o, do [B,H,Nq,D], k, v [B,H,Nk,D], lse
     fp32 [B,H,Nq] (the forward's, same scale and causal flag). Returns
@@ -180,9 +230,14 @@ def fa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tens
         _check_tensor(name, t, torch.bfloat16)
         if tuple(t.shape) != tuple(ref.shape):
             raise ValueError(f"{name} must have the shape {tuple(ref.shape)}")
-    code = _lib.load().fa_backward(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
-        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), ws_bytes,
-        B, H, Nq, Nk, D, float(scale), int(bool(causal)), _stream(q))
+    mode = _causal_mode(causal)
+    kv_lens = _check_kv_lens(kv_lens, B, q.device)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr())
+    outs = (dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), ws_bytes)
+    if kv_lens is None:
+        code = _lib.load().fa_backward(*ptrs, *outs, B, H, Nq, Nk, D, float(scale), mode, _stream(q))
+    else:
+        code = _lib.load().fa_backward_masked(*ptrs, kv_lens.data_ptr(), *outs, B, H, Nq, Nk, D, float(scale),
+                                              mode, _stream(q))
     _lib.check(code, "fa_backward")
     return dq, dk, dv

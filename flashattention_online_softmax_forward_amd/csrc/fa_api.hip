@@ -9,6 +9,10 @@
 #include "fa.h"
 #include "fa_internal.h"
 
+static_assert(FA_CAUSAL_NONE == fa::kCausalNone && FA_CAUSAL_TOP_LEFT == fa::kCausalTopLeft &&
+                  FA_CAUSAL_BOTTOM_RIGHT == fa::kCausalBottomRight,
+              "causal modes of the C ABI and the kernels agree");
+
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -21,6 +25,17 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 bool good_scale(float s) { return std::isfinite(s) && s > 0.0f; }
+
+bool good_causal(int c) { return c == FA_CAUSAL_NONE || c == FA_CAUSAL_TOP_LEFT || c == FA_CAUSAL_BOTTOM_RIGHT; }
+
+// kv_lens (NULL or B ints, 4-byte aligned) must not overlap the call's two
+// largest outputs (it is read while they are written).
+bool good_kv_lens(const int* kv_lens, int B, const void* out1, size_t n1, const void* out2, size_t n2) {
+    if (!kv_lens) return true;
+    if (!aligned4(kv_lens)) return false;
+    const size_t nb = (size_t)B * sizeof(int);
+    return !overlaps(kv_lens, nb, out1, n1) && !overlaps(kv_lens, nb, out2, n2);
+}
 
 // Shared checks of the two forward entry points; `elem` is the element size.
 fa_status check_forward(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
@@ -63,22 +78,40 @@ const char* fa_status_string(fa_status s) {
     return "FA_ERR_UNKNOWN: unknown status code";
 }
 
-fa_status fa_forward(const void* Q, const void* K, const void* V, void* O, float* LSE,
-                     int B, int H, int Nq, int Nk, int D, float scale, int causal, hipStream_t stream) {
+fa_status fa_forward_masked(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                            const int* kv_lens, int B, int H, int Nq, int Nk, int D, float scale, int causal,
+                            hipStream_t stream) {
+    if (!good_causal(causal)) return FA_ERR_INVALID_ARG;
     bool nothing = false;
     const fa_status st = check_forward(Q, K, V, O, LSE, B, H, Nq, Nk, D, scale, 2, fa::BM_FWD, &nothing);
     if (st != FA_OK || nothing) return st;
-    const fa::FwdArgs a{Q, K, V, O, LSE, B, H, Nq, Nk, D, scale, causal != 0, stream};
+    if (!good_kv_lens(kv_lens, B, O, (size_t)B * H * Nq * D * 2, LSE, (size_t)B * H * Nq * 4))
+        return FA_ERR_INVALID_ARG;
+    const fa::FwdArgs a{Q, K, V, O, LSE, kv_lens, B, H, Nq, Nk, D, scale, causal, stream};
     return fa::launch_fwd_bf16(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+fa_status fa_forward(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                     int B, int H, int Nq, int Nk, int D, float scale, int causal, hipStream_t stream) {
+    return fa_forward_masked(Q, K, V, O, LSE, nullptr, B, H, Nq, Nk, D, scale, causal, stream);
+}
+
+fa_status fa_forward_f32_masked(const float* Q, const float* K, const float* V, float* O, float* LSE,
+                                const int* kv_lens, int B, int H, int Nq, int Nk, int D, float scale,
+                                int causal, hipStream_t stream) {
+    if (!good_causal(causal)) return FA_ERR_INVALID_ARG;
+    bool nothing = false;
+    const fa_status st = check_forward(Q, K, V, O, LSE, B, H, Nq, Nk, D, scale, 4, fa::BM_FWD_F32, &nothing);
+    if (st != FA_OK || nothing) return st;
+    if (!good_kv_lens(kv_lens, B, O, (size_t)B * H * Nq * D * 4, LSE, (size_t)B * H * Nq * 4))
+        return FA_ERR_INVALID_ARG;
+    const fa::FwdArgs a{Q, K, V, O, LSE, kv_lens, B, H, Nq, Nk, D, scale, causal, stream};
+    return fa::launch_fwd_f32(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 fa_status fa_forward_f32(const float* Q, const float* K, const float* V, float* O, float* LSE,
                          int B, int H, int Nq, int Nk, int D, float scale, int causal, hipStream_t stream) {
-    bool nothing = false;
-    const fa_status st = check_forward(Q, K, V, O, LSE, B, H, Nq, Nk, D, scale, 4, fa::BM_FWD_F32, &nothing);
-    if (st != FA_OK || nothing) return st;
-    const fa::FwdArgs a{Q, K, V, O, LSE, B, H, Nq, Nk, D, scale, causal != 0, stream};
-    return fa::launch_fwd_f32(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+    return fa_forward_f32_masked(Q, K, V, O, LSE, nullptr, B, H, Nq, Nk, D, scale, causal, stream);
 }
 
 size_t fa_decode_workspace_bytes(int B, int H, int D, int num_splits) {
@@ -86,9 +119,9 @@ size_t fa_decode_workspace_bytes(int B, int H, int D, int num_splits) {
     return (size_t)B * H * num_splits * (D + 2) * sizeof(float);
 }
 
-fa_status fa_decode_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE,
-                            void* workspace, size_t workspace_bytes, int B, int H, int Nk, int D,
-                            float scale, int num_splits, hipStream_t stream) {
+fa_status fa_decode_splitkv_masked(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                                   const int* kv_lens, void* workspace, size_t workspace_bytes, int B, int H,
+                                   int Nk, int D, float scale, int num_splits, hipStream_t stream) {
     if (B < 0 || H < 0 || Nk < 0 || num_splits < 1) return FA_ERR_INVALID_ARG;
     if (!good_scale(scale)) return FA_ERR_INVALID_ARG;
     if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
@@ -109,11 +142,20 @@ fa_status fa_decode_splitkv(const void* Q, const void* K, const void* V, void* O
         overlaps(workspace, need, V, bytes_kv) || overlaps(workspace, need, O, bytes_q) ||
         overlaps(workspace, need, LSE, (size_t)B * H * 4))
         return FA_ERR_INVALID_ARG;
-    const int chunk = (int)(((long long)Nk + num_splits - 1) / num_splits);
+    if (!good_kv_lens(kv_lens, B, O, bytes_q, LSE, (size_t)B * H * 4) ||
+        overlaps(kv_lens, (size_t)B * 4, workspace, need))
+        return FA_ERR_INVALID_ARG;
     float* ws_o = static_cast<float*>(workspace);
     float* ws_ml = ws_o + (size_t)B * H * num_splits * D;
-    const fa::DecodeArgs a{Q, K, V, O, LSE, ws_o, ws_ml, B, H, Nk, D, num_splits, chunk, scale, stream};
+    const fa::DecodeArgs a{Q, K, V, O, LSE, ws_o, ws_ml, kv_lens, B, H, Nk, D, num_splits, scale, stream};
     return fa::launch_decode(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+fa_status fa_decode_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                            void* workspace, size_t workspace_bytes, int B, int H, int Nk, int D,
+                            float scale, int num_splits, hipStream_t stream) {
+    return fa_decode_splitkv_masked(Q, K, V, O, LSE, nullptr, workspace, workspace_bytes, B, H, Nk, D, scale,
+                                    num_splits, stream);
 }
 
 size_t fa_backward_workspace_bytes(int B, int H, int Nq) {
@@ -121,12 +163,12 @@ size_t fa_backward_workspace_bytes(int B, int H, int Nq) {
     return (size_t)B * H * Nq * sizeof(float);
 }
 
-fa_status fa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
-                      const float* LSE, void* dQ, void* dK, void* dV, void* workspace,
-                      size_t workspace_bytes, int B, int H, int Nq, int Nk, int D, float scale,
-                      int causal, hipStream_t stream) {
+fa_status fa_backward_masked(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                             const float* LSE, const int* kv_lens, void* dQ, void* dK, void* dV, void* workspace,
+                             size_t workspace_bytes, int B, int H, int Nq, int Nk, int D, float scale,
+                             int causal, hipStream_t stream) {
     if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return FA_ERR_INVALID_ARG;
-    if (!good_scale(scale)) return FA_ERR_INVALID_ARG;
+    if (!good_scale(scale) || !good_causal(causal)) return FA_ERR_INVALID_ARG;
     if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
     if ((long long)B * H == 0 || ((long long)Nq == 0 && Nk == 0)) return FA_OK;
     if (Nk < 1) return FA_ERR_INVALID_ARG;
@@ -139,6 +181,7 @@ fa_status fa_backward(const void* Q, const void* K, const void* V, const void* O
         if (overlaps(dK, bkv, dV, bkv) || overlaps(dK, bkv, K, bkv) || overlaps(dK, bkv, V, bkv) ||
             overlaps(dV, bkv, K, bkv) || overlaps(dV, bkv, V, bkv))
             return FA_ERR_INVALID_ARG;
+        if (!good_kv_lens(kv_lens, B, dK, bkv, dV, bkv)) return FA_ERR_INVALID_ARG;
     } else {
         if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV || !workspace) return FA_ERR_INVALID_ARG;
         if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) ||
@@ -160,10 +203,21 @@ fa_status fa_backward(const void* Q, const void* K, const void* V, const void* O
             for (int j = i + 1; j < 4; ++j)
                 if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return FA_ERR_INVALID_ARG;
         }
+        if (!good_kv_lens(kv_lens, B, dQ, bq, dK, bkv) || overlaps(kv_lens, (size_t)B * 4, dV, bkv) ||
+            overlaps(kv_lens, (size_t)B * 4, workspace, need))
+            return FA_ERR_INVALID_ARG;
     }
-    const fa::BwdArgs a{Q, K, V, O, dO, LSE, dQ, dK, dV, static_cast<float*>(workspace),
-                        B, H, Nq, Nk, D, scale, causal != 0, stream};
+    const fa::BwdArgs a{Q, K, V, O, dO, LSE, dQ, dK, dV, static_cast<float*>(workspace), kv_lens,
+                        B, H, Nq, Nk, D, scale, causal, stream};
     return fa::launch_bwd(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+fa_status fa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                      const float* LSE, void* dQ, void* dK, void* dV, void* workspace,
+                      size_t workspace_bytes, int B, int H, int Nq, int Nk, int D, float scale,
+                      int causal, hipStream_t stream) {
+    return fa_backward_masked(Q, K, V, O, dO, LSE, nullptr, dQ, dK, dV, workspace, workspace_bytes, B, H, Nq,
+                              Nk, D, scale, causal, stream);
 }
 
 }  // extern "C"

@@ -28,9 +28,12 @@
 //     transposed (8-byte transpose reads of 4 consecutive rows). One XOR
 //     swizzle of the 16-byte chunks makes both patterns free of LDS bank
 //     conflicts, so each tile is staged once.
-//   * Masking: causal (key j visible from query i iff j <= i), keys past Nk
-//     and queries past Nq get P = 0 (so dS = 0 too); rows past the end are
-//     loaded clamped to the last row and never stored.
+//   * Masking: causal (key j visible from query i iff j <= i + off, off = 0
+//     top-left or Lk - Nq bottom-right), padding keys (past the batch entry's
+//     real key count Lk) and queries past Nq get P = 0 (so dS = 0 too); rows
+//     past the end are loaded clamped to the last row and never stored. A
+//     query row with no visible key (LSE = -inf) only ever meets masked pairs,
+//     so its P is forced to 0 before exp2(+inf) can be used; its dQ is 0.
 //   * dQ, dK, dV are accumulated in fp32 and rounded to bf16 once.
 
 #include "fa_device.h"
@@ -224,11 +227,11 @@ __global__ __launch_bounds__(kBwdThreads, 2)
 void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                    const uint16_t* __restrict__ Vg, const uint16_t* __restrict__ dOg,
                    const float* __restrict__ LSEg, const float* __restrict__ Dg,
-                   uint16_t* __restrict__ dQg, int Nq, int Nk, int nqb, float scale, float scale2,
-                   int causal) {
+                   uint16_t* __restrict__ dQg, const int* __restrict__ kv_lens, int H, int Nq, int Nk,
+                   int nqb, float scale, float scale2, int causal) {
     constexpr int NKK = D / 16, NDB = D / 32;
     constexpr int TILE = kBT * D;
-    const bool CAUSAL = causal != 0;
+    const bool CAUSAL = causal != kCausalNone;
 
     __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[TILE];
@@ -252,6 +255,8 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
 
     const uint16_t* K = Kg + (size_t)bh * Nk * D;
     const uint16_t* V = Vg + (size_t)bh * Nk * D;
+    const int Lk = real_keys(kv_lens, bh / H, Nk);
+    const int doff = causal == kCausalBottomRight ? Lk - Nq : 0;   // key j visible from query i iff j <= i + doff
 
     bf16x8_t qf[NKK], dof[NKK];
     load_b_rows<D>(Qg + (size_t)bh * Nq * D, qrow, qvalid, h, qf);
@@ -268,15 +273,16 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-    int kend = Nk;
-    if (CAUSAL) kend = min(Nk, min(q0 + BM_BWD, Nq));
+    int kend = Lk;
+    if (CAUSAL) kend = max(0, min(Lk, min(q0 + BM_BWD, Nq) + doff));
     const int ntiles = (kend + kBT - 1) / kBT;
-    const int my_tiles = CAUSAL ? min(ntiles, (wrow0 + 31) / kBT + 1) : ntiles;
+    const int wlast = wrow0 + 31 + doff;        // last key the wave's last row may see
+    const int my_tiles = CAUSAL ? (wlast < 0 ? 0 : min(ntiles, wlast / kBT + 1)) : ntiles;
 
     auto stage = [&](int t, uint16_t* kd, uint16_t* vd) __attribute__((always_inline)) {
-        const int kv0 = t * kBT;
-        stage_rows<D>(K + (size_t)kv0 * D, kBT, Nk - 1 - kv0, kd, wave, lane);
-        stage_rows<D>(V + (size_t)kv0 * D, kBT, Nk - 1 - kv0, vd, wave, lane);
+        const int kv0 = t * kBT;               // < kend <= Lk, so the clamp row is real
+        stage_rows<D>(K + (size_t)kv0 * D, kBT, Lk - 1 - kv0, kd, wave, lane);
+        stage_rows<D>(V + (size_t)kv0 * D, kBT, Lk - 1 - kv0, vd, wave, lane);
     };
     auto compute = [&](int t, const uint16_t* kt, const uint16_t* vt) __attribute__((always_inline)) {
         // S^T = K Q^T and dP^T = V dO^T for 32 keys x this wave's 32 queries.
@@ -287,7 +293,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(vt, off, kk), dof[kk], dp, 0, 0, 0);
         }
         const int kv0 = t * kBT;
-        const bool edge = kv0 + kBT > Nk || (CAUSAL && kv0 + kBT - 1 > wrow0);
+        const bool edge = kv0 + kBT > Lk || (CAUSAL && kv0 + kBT - 1 > wrow0 + doff);
         bf16x8_t dsf[2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -298,7 +304,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
                 float p = exp2_hw(__builtin_fmaf(s[r], scale2, -l2));
                 if (edge) {
                     const int key = kv0 + tt * 16 + h * 8 + e;
-                    if (key >= Nk || (CAUSAL && key > qrow)) p = 0.f;
+                    if (key >= Lk || (CAUSAL && key > qrow + doff)) p = 0.f;
                 }
                 ds[e] = p * (dp[r] - dr);
             }
@@ -317,7 +323,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
                 acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(kt, off, tt, db), dsf[tt], acc[db], 0, 0, 0);
     };
 
-    stage(0, k_lds0, v_lds0);
+    if (ntiles > 0) stage(0, k_lds0, v_lds0);
     lds_dma_wait_all();
     __syncthreads();
     // Tile t in buffer t % 2; the next tile is loaded while t is computed and
@@ -343,11 +349,11 @@ __global__ __launch_bounds__(kBwdThreads, 2)
 void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                      const uint16_t* __restrict__ Vg, const uint16_t* __restrict__ dOg,
                      const float* __restrict__ LSEg, const float* __restrict__ Dg,
-                     uint16_t* __restrict__ dKg, uint16_t* __restrict__ dVg, int Nq, int Nk, int nkb,
-                     float scale, float scale2, int causal) {
+                     uint16_t* __restrict__ dKg, uint16_t* __restrict__ dVg, const int* __restrict__ kv_lens,
+                     int H, int Nq, int Nk, int nkb, float scale, float scale2, int causal) {
     constexpr int NKK = D / 16, NDB = D / 32, CPR = D / 8;
     constexpr int TILE = kBT * D;
-    const bool CAUSAL = causal != 0;
+    const bool CAUSAL = causal != kCausalNone;
 
     // Small arrays first: every buffer's base then fits the 16-bit offset
     // field of the LDS instructions.
@@ -371,6 +377,8 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     const int kw0 = k0 + wave * 32;
     const int krow = kw0 + j;
     const bool kvalid = krow < Nk;
+    const int Lk = real_keys(kv_lens, bh / H, Nk);
+    const int doff = causal == kCausalBottomRight ? Lk - Nq : 0;   // key j visible from query i iff j <= i + doff
 
     const uint16_t* Q = Qg + (size_t)bh * Nq * D;
     const uint16_t* dO = dOg + (size_t)bh * Nq * D;
@@ -401,10 +409,15 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
         }
 
     const int nqt = (Nq + kBT - 1) / kBT;
-    // Causal: queries i >= key j only, so tiles start at the block's (the
-    // wave's) first key.
-    const int first = CAUSAL ? min(nqt, k0 / kBT) : 0;
-    const int my_first = CAUSAL ? min(nqt, kw0 / kBT) : 0;
+    // Causal: key j is seen by queries i >= j - off only, so tiles start at the
+    // block's (the wave's) first such query. Keys at or past Lk are padding:
+    // a block (a wave) made of them runs no tile and stores zeros.
+    auto first_tile = [&](int key0) __attribute__((always_inline)) {
+        if (key0 >= Lk) return nqt;
+        return CAUSAL ? min(nqt, max(0, key0 - doff) / kBT) : 0;
+    };
+    const int first = first_tile(k0);
+    const int my_first = first_tile(kw0);
 
     // L and D of tile u through registers of wave 0 (lanes 0-31: L, 32-63: D).
     float ld_reg = 0.f;
@@ -433,7 +446,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
         mfma_stream<NKK, LEAD>([&](int kk) { return row_operand<D>(qt, off, kk); },
                                [&](int kk, bf16x8_t a) { s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[kk], s, 0, 0, 0); });
         const int q0 = u * kBT;
-        const bool edge = q0 + kBT > Nq || (CAUSAL && q0 < kw0 + 31);
+        const bool edge = q0 + kBT > Nq || kw0 + 32 > Lk || (CAUSAL && q0 + doff < kw0 + 31);
         // P (fp32, kept for dS) and its bf16 copy. Register r of lane (j, h)
         // is query 16*(r/8) + 8*h + r%8 of the tile.
         bf16x8_t pf[2];
@@ -447,7 +460,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
                 float p = exp2_hw(__builtin_fmaf(s[r], scale2, -(e < 4 ? la[e] : lb[e - 4])));
                 if (edge) {
                     const int q = q0 + tt * 16 + h * 8 + e;
-                    if (q >= Nq || (CAUSAL && q < krow)) p = 0.f;
+                    if (q >= Nq || krow >= Lk || (CAUSAL && q + doff < krow)) p = 0.f;
                 }
                 s[r] = p;
             }
@@ -542,8 +555,8 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
         const int nqb = (a.Nq + BM_BWD - 1) / BM_BWD;
         hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3(a.B * a.H * nqb), dim3(kBwdThreads), 0, a.stream,
                            (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
-                           (const uint16_t*)a.dO, a.LSE, a.Dvec, (uint16_t*)a.dQ, a.Nq, a.Nk, nqb,
-                           a.scale, scale2, a.causal);
+                           (const uint16_t*)a.dO, a.LSE, a.Dvec, (uint16_t*)a.dQ, a.kv_lens, a.H, a.Nq, a.Nk,
+                           nqb, a.scale, scale2, a.causal);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -552,8 +565,8 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
     const int nkb = (a.Nk + BM_BWD - 1) / BM_BWD;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(a.B * a.H * nkb), dim3(kBwdThreads), 0, a.stream,
                        (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
-                       (const uint16_t*)a.dO, a.LSE, a.Dvec, (uint16_t*)a.dK, (uint16_t*)a.dV,
-                       a.Nq, a.Nk, nkb, a.scale, scale2, a.causal);
+                       (const uint16_t*)a.dO, a.LSE, a.Dvec, (uint16_t*)a.dK, (uint16_t*)a.dV, a.kv_lens,
+                       a.H, a.Nq, a.Nk, nkb, a.scale, scale2, a.causal);
     return hipGetLastError();
 }
 

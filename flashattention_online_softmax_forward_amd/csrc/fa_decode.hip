@@ -16,6 +16,10 @@
 // partials with the same rule, M = max m_s, l = sum l_s 2^(m_s - M),
 // o = sum o_s 2^(m_s - M), and writes O = o / l (bf16) and
 // LSE = (M + log2 l) ln 2. Empty chunks carry (-inf, 0, 0) and weigh nothing.
+//
+// Key padding: batch entry b has Lk = kv_lens[b] real keys (all Nk without
+// kv_lens), split into S chunks of ceil(Lk / S) keys. A cache with no real key
+// has only empty chunks and gets O = 0, LSE = -inf.
 
 #include "fa_device.h"
 #include "fa_internal.h"
@@ -29,7 +33,8 @@ template <int D>
 __global__ __launch_bounds__(kDecThreads)
 void decode_partial_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                            const uint16_t* __restrict__ Vg, float* __restrict__ ws_o,
-                           float* __restrict__ ws_ml, int Nk, int S, int chunk, float scale2) {
+                           float* __restrict__ ws_ml, const int* __restrict__ kv_lens, int H, int Nk, int S,
+                           float scale2) {
     constexpr int LPK = D / 8;                 // lanes per key row
     constexpr int G = kDecThreads / LPK;       // key groups per workgroup
     constexpr int U = kDecUnroll;
@@ -44,9 +49,11 @@ void decode_partial_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __re
     const int split = blockIdx.x % S;
     const int bh = blockIdx.x / S;
 
+    const int Lk = real_keys(kv_lens, bh / H, Nk);
+    const int chunk = (int)(((long long)Lk + S - 1) / S);
     const long long jb = (long long)split * chunk;
-    const int j0 = (int)(jb < Nk ? jb : Nk);
-    const int j1 = (int)(jb + chunk < Nk ? jb + chunk : Nk);
+    const int j0 = (int)(jb < Lk ? jb : Lk);
+    const int j1 = (int)(jb + chunk < Lk ? jb + chunk : Lk);
 
     const uint16_t* K = Kg + (size_t)bh * Nk * D + sub * 8;
     const uint16_t* V = Vg + (size_t)bh * Nk * D + sub * 8;
@@ -207,8 +214,9 @@ void decode_combine_kernel(const float* __restrict__ ws_o, const float* __restri
             lt += sm_l[g];
             ot += sm_o[g * D + tid];
         }
-        Og[(size_t)bh * D + tid] = __builtin_bit_cast(uint16_t, (__bf16)(ot / lt));
-        if (tid == 0 && LSEg) LSEg[bh] = (M + __log2f(lt)) * kLn2;
+        // No real key at all (every chunk empty): O = 0, LSE = -inf.
+        Og[(size_t)bh * D + tid] = __builtin_bit_cast(uint16_t, (__bf16)(lt > 0.f ? ot / lt : 0.f));
+        if (tid == 0 && LSEg) LSEg[bh] = lt > 0.f ? (M + __log2f(lt)) * kLn2 : -INFINITY;
     }
 }
 
@@ -217,7 +225,7 @@ static hipError_t launch_d(const DecodeArgs& a) {
     const int BH = a.B * a.H;
     hipLaunchKernelGGL((decode_partial_kernel<D>), dim3(BH * a.S), dim3(kDecThreads), 0, a.stream,
                        (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V, a.ws_o, a.ws_ml,
-                       a.Nk, a.S, a.chunk, a.scale * kLog2e);
+                       a.kv_lens, a.H, a.Nk, a.S, a.scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(BH), dim3(kCombThreads), 0, a.stream, a.ws_o,

@@ -15,6 +15,10 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// Running maximum of a row that has not seen a visible key yet (base 2). Finite,
+// so exp2(masked score - it) = exp2(-inf) = 0 and exp2(it - real maximum) = 0,
+// where -inf would give exp2(-inf - -inf) = NaN.
+constexpr float kNoKeyMax = -1e30f;
 
 // Two fp32 values to a packed pair of bf16 (round to nearest even: one
 // v_cvt_pk_bf16_f32 on gfx950).

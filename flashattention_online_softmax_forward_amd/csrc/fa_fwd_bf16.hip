@@ -48,6 +48,15 @@
 //   * Causal: key tiles past the block's last row are never visited, tiles a
 //     whole wave cannot see are skipped by that wave, masks are applied only on
 //     diagonal and ragged tiles, and the heaviest query blocks are issued first.
+//     Top-left alignment shows key j to query i iff j <= i; bottom-right iff
+//     j <= i + (Lk - Nq), one diagonal offset in every bound and mask.
+//   * Key padding: batch entry b has Lk = kv_lens[b] real keys (all Nk without
+//     kv_lens); keys past Lk are never loaded or are masked like a ragged tail.
+//   * Fully masked rows (bottom-right rows before the first key, or Lk = 0):
+//     the running maximum starts at a large finite negative value instead of
+//     -inf (the Pitfalls passage of the ML compiler page: exp2(-inf - -inf)
+//     would be NaN), so a masked score gives exp2(-inf) = 0 and a row that
+//     never sees a key ends with l = 0; it is written as O = 0, LSE = -inf.
 
 #include "fa_device.h"
 #include "fa_internal.h"
@@ -90,10 +99,11 @@ template <int D>
 __global__ __launch_bounds__(kFwdThreads, 1)
 void fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                      const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
-                     float* __restrict__ LSEg, int Nq, int Nk, int nqb, float scale2, int causal) {
-    // The causal flag is a uniform run-time argument rather than a template
-    // parameter: one code shape for both keeps register allocation stable.
-    const bool CAUSAL = causal != 0;
+                     float* __restrict__ LSEg, const int* __restrict__ kv_lens, int H, int Nq, int Nk,
+                     int nqb, float scale2, int causal) {
+    // The causal mode is a uniform run-time argument rather than a template
+    // parameter: one code shape for all keeps register allocation stable.
+    const bool CAUSAL = causal != kCausalNone;
     constexpr int BN = Bf16Tile<D>::BN;
     constexpr int TILE = BN * D;               // elements of one K (or V) tile
     constexpr int NCB = BN / 32;               // 32-key blocks of S^T
@@ -130,6 +140,9 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     const uint16_t* Q = Qg + (size_t)bh * Nq * D;
     const uint16_t* K = Kg + (size_t)bh * Nk * D;
     const uint16_t* V = Vg + (size_t)bh * Nk * D;
+    const int Lk = real_keys(kv_lens, bh / H, Nk);
+    // Causal diagonal offset: key j is visible from query i iff j <= i + off.
+    const int off = causal == kCausalBottomRight ? Lk - Nq : 0;
 
     const int wrow0 = q0 + wave * 32;
     const int qrow = wrow0 + j;
@@ -143,11 +156,12 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
         qf[kk] = __builtin_bit_cast(bf16x8_t, w);
     }
 
-    int kend = Nk;
-    if (CAUSAL) kend = min(Nk, min(q0 + BM_FWD, Nq));
+    int kend = Lk;
+    if (CAUSAL) kend = max(0, min(Lk, min(q0 + BM_FWD, Nq) + off));
     const int ntiles = (kend + BN - 1) / BN;
     // Tiles this wave computes: a causal tile entirely after all its rows is skipped.
-    const int my_tiles = CAUSAL ? min(ntiles, (wrow0 + 31) / BN + 1) : ntiles;
+    const int wlast = wrow0 + 31 + off;        // last key the wave's last row may see
+    const int my_tiles = CAUSAL ? (wlast < 0 ? 0 : min(ntiles, wlast / BN + 1)) : ntiles;
 
     // DMA slots (group 0 only): chunk p = (i*4 + wave)*64 + lane of a tile
     // lands at byte 16*p of the LDS tile and holds logical chunk
@@ -162,7 +176,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
         ld_vcol[i] = ((p % CPR) ^ v_swz<CPR>(ld_row[i])) * 8;
     }
     auto dma = [&](const uint16_t* src, const int* col, int kv0, uint16_t* dst) __attribute__((always_inline)) {
-        const int last = Nk - 1 - kv0;
+        const int last = Lk - 1 - kv0;           // >= 0: only tiles below kend <= Lk are loaded
         const uint16_t* base = src + (size_t)kv0 * D;
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
@@ -181,7 +195,9 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     f32x16_t s[NCB];            // S^T of the tile between its MFMA step and its softmax step
     bf16x8_t pf[NPV];           // P of the tile between its softmax step and its PV step
 
-    float m_run = -INFINITY;   // base-2 scaled maximum the row is accumulated against
+    // Base-2 scaled maximum the row is accumulated against; kNoKeyMax until the
+    // row's first visible key (finite, so masked scores give exp2(-inf) = 0).
+    float m_run = kNoKeyMax;
     float l_run = 0.f;         // this lane's half of the running sum
 
     const int srow = s_row_perm(j);
@@ -264,15 +280,15 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     auto step_softmax = [&](int t) __attribute__((always_inline)) {
         if (t < 0 || t >= my_tiles) return;
         const int kv0 = t * BN;
-        const bool ragged = kv0 + BN > Nk;
-        const bool diag = CAUSAL && (kv0 + BN - 1 > wrow0);
+        const bool ragged = kv0 + BN > Lk;
+        const bool diag = CAUSAL && (kv0 + BN - 1 > wrow0 + off);
         if (ragged || diag) {
 #pragma unroll
             for (int c = 0; c < NCB; ++c)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = kv0 + c * 32 + (r >> 3) * 16 + h * 8 + (r & 7);
-                    const bool dead = key >= Nk || (CAUSAL && key > qrow);
+                    const bool dead = key >= Lk || (CAUSAL && key > qrow + off);
                     if (dead) s[c][r] = -INFINITY;
                 }
         }
@@ -363,7 +379,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    if (loader) dma(K, ld_kcol, 0, k_lds0);
+    if (loader && ntiles > 0) dma(K, ld_kcol, 0, k_lds0);
     __builtin_amdgcn_s_waitcnt(0xF70);
     __syncthreads();
     if (!loader) __builtin_amdgcn_s_barrier();
@@ -376,10 +392,11 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     }
     if (loader) __builtin_amdgcn_s_barrier();
 
-    // Epilogue: O / l to bf16, LSE = (m + log2 l) * ln 2.
+    // Epilogue: O / l to bf16, LSE = (m + log2 l) * ln 2; a row that saw no
+    // key (l = 0, O = 0) gets O = 0 and LSE = -inf.
     const float l_tot = sum_xor32(l_run);
     if (qrow < Nq) {
-        const float inv = 1.0f / l_tot;
+        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
         uint16_t* orow = Og + ((size_t)bh * Nq + qrow) * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -391,7 +408,8 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
                 w[1] = pack_bf16x2(acc_o[db][a4 * 4 + 2] * inv, acc_o[db][a4 * 4 + 3] * inv);
                 *(u32x2_t*)(orow + d) = w;
             }
-        if (h == 0 && LSEg) LSEg[(size_t)bh * Nq + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+        if (h == 0 && LSEg)
+            LSEg[(size_t)bh * Nq + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
     }
 }
 
@@ -401,7 +419,7 @@ static hipError_t launch_one(const FwdArgs& a) {
     const int grid = a.B * a.H * nqb;
     hipLaunchKernelGGL((fwd_bf16_kernel<D>), dim3(grid), dim3(kFwdThreads), 0, a.stream,
                        (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
-                       (uint16_t*)a.O, a.LSE, a.Nq, a.Nk, nqb, a.scale * kLog2e, a.causal);
+                       (uint16_t*)a.O, a.LSE, a.kv_lens, a.H, a.Nq, a.Nk, nqb, a.scale * kLog2e, a.causal);
     return hipGetLastError();
 }
 

@@ -7,7 +7,10 @@
 // Q, the K and V tiles and the P tile sit in LDS; each thread computes 16
 // scores of its row, the row max / sum are reduced over the 4 threads with DPP,
 // and each thread accumulates a quarter of the row's output (D/4 values in
-// VGPRs). Base-2 exponentials with log2(e) folded into the scale.
+// VGPRs). Base-2 exponentials with log2(e) folded into the scale. Masks as in
+// the bf16 kernel: key padding (kv_lens), top-left or bottom-right causal
+// alignment (one diagonal offset), and rows with no visible key written as
+// O = 0, LSE = -inf (the running maximum starts finite, kNoKeyMax).
 
 #include "fa_device.h"
 #include "fa_internal.h"
@@ -21,7 +24,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kF32Threads)
 void fwd_f32_kernel(const float* __restrict__ Qg, const float* __restrict__ Kg,
                     const float* __restrict__ Vg, float* __restrict__ Og,
-                    float* __restrict__ LSEg, int Nq, int Nk, int nqb, float scale2) {
+                    float* __restrict__ LSEg, const int* __restrict__ kv_lens, int H, int Nq, int Nk,
+                    int nqb, float scale2, int bottom_right) {
     constexpr int BM = BM_FWD_F32;
     constexpr int BN = kF32BN;
     constexpr int P = D + 4;           // row pitch of Q/K/V tiles (floats)
@@ -48,6 +52,8 @@ void fwd_f32_kernel(const float* __restrict__ Qg, const float* __restrict__ Kg,
     const float* Q = Qg + (size_t)bh * Nq * D;
     const float* K = Kg + (size_t)bh * Nk * D;
     const float* V = Vg + (size_t)bh * Nk * D;
+    const int Lk = real_keys(kv_lens, bh / H, Nk);
+    const int off = bottom_right ? Lk - Nq : 0;    // key j visible from query i iff j <= i + off
 
     for (int c = tid; c < BM * C4; c += kF32Threads) {
         const int row = c / C4, col = c % C4;
@@ -56,14 +62,14 @@ void fwd_f32_kernel(const float* __restrict__ Qg, const float* __restrict__ Kg,
         *(f32x4_t*)(Qs + row * P + col * 4) = w;
     }
 
-    int kend = Nk;
-    if (CAUSAL) kend = min(Nk, min(q0 + BM, Nq));
+    int kend = Lk;
+    if (CAUSAL) kend = max(0, min(Lk, min(q0 + BM, Nq) + off));
     const int ntiles = (kend + BN - 1) / BN;
 
     f32x4_t o[NE];
 #pragma unroll
     for (int e = 0; e < NE; ++e) o[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY;
+    float m_run = kNoKeyMax;
     float l_run = 0.f;                 // this thread's quarter of the row sum
 
     for (int t = 0; t < ntiles; ++t) {
@@ -73,7 +79,7 @@ void fwd_f32_kernel(const float* __restrict__ Qg, const float* __restrict__ Kg,
             const int row = c / C4, col = c % C4;
             const int key = kv0 + row;
             f32x4_t kw = {0.f, 0.f, 0.f, 0.f}, vw = {0.f, 0.f, 0.f, 0.f};
-            if (key < Nk) {
+            if (key < Lk) {
                 kw = *(const f32x4_t*)(K + (size_t)key * D + col * 4);
                 vw = *(const f32x4_t*)(V + (size_t)key * D + col * 4);
             }
@@ -101,7 +107,7 @@ void fwd_f32_kernel(const float* __restrict__ Qg, const float* __restrict__ Kg,
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int key = kv0 + sub + 4 * i;
-            if (key >= Nk || (CAUSAL && key > qrow)) s[i] = -INFINITY;
+            if (key >= Lk || (CAUSAL && key > qrow + off)) s[i] = -INFINITY;
             mx = fmaxf(mx, s[i]);
         }
         mx = group_max<4>(mx);
@@ -135,11 +141,12 @@ void fwd_f32_kernel(const float* __restrict__ Qg, const float* __restrict__ Kg,
 
     const float l_tot = group_sum<4>(l_run);
     if (qrow < Nq) {
-        const float inv = 1.0f / l_tot;
+        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
         float* orow = Og + ((size_t)bh * Nq + qrow) * D;
 #pragma unroll
         for (int e = 0; e < NE; ++e) *(f32x4_t*)(orow + sub * 4 + e * 16) = o[e] * inv;
-        if (sub == 0 && LSEg) LSEg[(size_t)bh * Nq + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+        if (sub == 0 && LSEg)
+            LSEg[(size_t)bh * Nq + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
     }
 }
 
@@ -149,7 +156,8 @@ static hipError_t launch_one(const FwdArgs& a) {
     const int grid = a.B * a.H * nqb;
     hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3(grid), dim3(kF32Threads), 0, a.stream,
                        (const float*)a.Q, (const float*)a.K, (const float*)a.V, (float*)a.O, a.LSE,
-                       a.Nq, a.Nk, nqb, a.scale * kLog2e);
+                       a.kv_lens, a.H, a.Nq, a.Nk, nqb, a.scale * kLog2e,
+                       (int)(a.causal == kCausalBottomRight));
     return hipGetLastError();
 }
 

@@ -10,15 +10,27 @@ constexpr int BM_FWD = 256;      // query rows per workgroup, bf16 forward (8 wa
 constexpr int BM_FWD_F32 = 64;   // query rows per workgroup, fp32 forward
 constexpr int BM_BWD = 128;      // rows (queries for dQ, keys for dK/dV) per workgroup, backward (4 waves x 32)
 
+// Causal alignment: none, top-left (key j visible from query i iff j <= i),
+// bottom-right (iff j <= i + Lk - Nq, Lk the batch entry's real key count).
+constexpr int kCausalNone = 0;
+constexpr int kCausalTopLeft = 1;
+constexpr int kCausalBottomRight = 2;
+
+// Real key count of batch entry b: kv_lens[b] clamped to [0, Nk], or Nk.
+__device__ __forceinline__ int real_keys(const int* kv_lens, int b, int Nk) {
+    return kv_lens ? min(max(kv_lens[b], 0), Nk) : Nk;
+}
+
 struct FwdArgs {
     const void* Q;
     const void* K;
     const void* V;
     void* O;
     float* LSE;
+    const int* kv_lens;   // [B] real key counts, or NULL (all Nk)
     int B, H, Nq, Nk, D;
     float scale;
-    int causal;
+    int causal;           // kCausalNone / kCausalTopLeft / kCausalBottomRight
     hipStream_t stream;
 };
 
@@ -30,7 +42,8 @@ struct DecodeArgs {
     float* LSE;
     float* ws_o;     // [B*H, S, D] partial unnormalised outputs
     float* ws_ml;    // [B*H, S, 2] partial (m in base 2, l)
-    int B, H, Nk, D, S, chunk;
+    const int* kv_lens;   // [B] real key counts, or NULL (all Nk)
+    int B, H, Nk, D, S;
     float scale;
     hipStream_t stream;
 };
@@ -46,9 +59,10 @@ struct BwdArgs {
     void* dK;
     void* dV;
     float* Dvec;     // [B*H, Nq] row dot products sum_d dO * O
+    const int* kv_lens;   // [B] real key counts, or NULL (all Nk)
     int B, H, Nq, Nk, D;
     float scale;
-    int causal;
+    int causal;           // kCausalNone / kCausalTopLeft / kCausalBottomRight
     hipStream_t stream;
 };
 

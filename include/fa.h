@@ -32,6 +32,19 @@
  *   - Errors are reported before anything is enqueued, except FA_ERR_LAUNCH,
  *     which reports hipGetLastError() after the launch. Calls are stateless and
  *     thread-safe.
+ *   - causal is one of fa_causal below; any other value is FA_ERR_INVALID_ARG.
+ *   - The *_masked variants add kv_lens: NULL, or a DEVICE array of B int32
+ *     giving the number of real keys of each batch entry; keys j >= kv_lens[b]
+ *     are padding and never attended (the padding masks of the Pitfalls
+ *     passage of the ML compiler page). Values are clamped to [0, Nk] on the
+ *     device (the library cannot read device memory before enqueueing).
+ *     kv_lens must be 4-byte aligned and must not overlap any output. Without
+ *     kv_lens every batch entry has Nk real keys.
+ *   - A query row that may attend no key at all (kv_lens[b] = 0, or the first
+ *     Nq - Lk rows under bottom-right alignment) has no softmax; it is written
+ *     as the empty sums the definition reduces to: O = 0 and LSE = -inf, and
+ *     its backward contributions are zero (the Pitfalls passage: such rows
+ *     must not produce NaN).
  */
 #ifndef FA_MI355X_H
 #define FA_MI355X_H
@@ -42,6 +55,20 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* Causal alignment. With Lk real keys (kv_lens[b], else Nk):
+ *   FA_CAUSAL_NONE:         every real key;
+ *   FA_CAUSAL_TOP_LEFT:     key j <= i (absolute indices from the first key,
+ *                           the rule of the exercise "Causal mask" on the ML
+ *                           compiler page and of phobos' causal_attention);
+ *   FA_CAUSAL_BOTTOM_RIGHT: key j <= i + (Lk - Nq), the last query aligned
+ *                           with the last real key (the queries are the newest
+ *                           Nq tokens); equal to top-left when Nq == Lk. */
+typedef enum fa_causal {
+    FA_CAUSAL_NONE = 0,
+    FA_CAUSAL_TOP_LEFT = 1,
+    FA_CAUSAL_BOTTOM_RIGHT = 2
+} fa_causal;
 
 typedef enum fa_status {
     FA_OK = 0,
@@ -54,10 +81,8 @@ typedef enum fa_status {
  * Prefill / full forward pass, bf16 in and out.
  *   Q: bf16 [B,H,Nq,D]; K, V: bf16 [B,H,Nk,D]; O: bf16 [B,H,Nq,D] (written);
  *   LSE: fp32 [B,H,Nq] (written) or NULL.
- *   causal != 0: query row i attends keys j <= i only (absolute indices counted
- *   from the first key, the rule of the exercise "Causal mask" on the ML
- *   compiler page and of phobos' causal_attention); keys past Nk are never
- *   attended (the masked last block of phobos' attention).
+ *   causal: an fa_causal value; keys past Nk are never attended (the masked
+ *   last block of phobos' attention).
  * Score and PV products use bf16 MFMA with fp32 accumulation; P is rounded to
  * bf16 before the PV product.
  */
@@ -65,6 +90,12 @@ fa_status fa_forward(const void* Q, const void* K, const void* V,
                      void* O, float* LSE,
                      int B, int H, int Nq, int Nk, int D,
                      float scale, int causal, hipStream_t stream);
+
+/* fa_forward with key padding: kv_lens as in the conventions above. */
+fa_status fa_forward_masked(const void* Q, const void* K, const void* V,
+                            void* O, float* LSE, const int* kv_lens,
+                            int B, int H, int Nq, int Nk, int D,
+                            float scale, int causal, hipStream_t stream);
 
 /*
  * The same operation in fp32 end to end (fp32 inputs, fp32 arithmetic, fp32
@@ -75,6 +106,12 @@ fa_status fa_forward_f32(const float* Q, const float* K, const float* V,
                          float* O, float* LSE,
                          int B, int H, int Nq, int Nk, int D,
                          float scale, int causal, hipStream_t stream);
+
+/* fa_forward_f32 with key padding: kv_lens as in the conventions above. */
+fa_status fa_forward_f32_masked(const float* Q, const float* K, const float* V,
+                                float* O, float* LSE, const int* kv_lens,
+                                int B, int H, int Nq, int Nk, int D,
+                                float scale, int causal, hipStream_t stream);
 
 /*
  * Bytes of device workspace fa_decode_splitkv needs: B*H*num_splits*(D+2)*4
@@ -104,6 +141,18 @@ fa_status fa_decode_splitkv(const void* Q, const void* K, const void* V,
                             void* workspace, size_t workspace_bytes,
                             int B, int H, int Nk, int D,
                             float scale, int num_splits, hipStream_t stream);
+
+/*
+ * fa_decode_splitkv over caches of different lengths: batch entry b attends
+ * its first Lk = kv_lens[b] keys (kv_lens as in the conventions above), split
+ * into num_splits chunks of ceil(Lk / num_splits) keys. Lk = 0 gives O = 0,
+ * LSE = -inf. kv_lens must not overlap the workspace either.
+ */
+fa_status fa_decode_splitkv_masked(const void* Q, const void* K, const void* V,
+                                   void* O, float* LSE, const int* kv_lens,
+                                   void* workspace, size_t workspace_bytes,
+                                   int B, int H, int Nk, int D,
+                                   float scale, int num_splits, hipStream_t stream);
 
 /*
  * Bytes of device workspace fa_backward needs: B*H*Nq*4 (one fp32 value per
@@ -142,6 +191,20 @@ fa_status fa_backward(const void* Q, const void* K, const void* V,
                       void* workspace, size_t workspace_bytes,
                       int B, int H, int Nq, int Nk, int D,
                       float scale, int causal, hipStream_t stream);
+
+/*
+ * fa_backward with key padding (kv_lens as in the conventions above; pass the
+ * kv_lens and causal of the forward call). Padding keys get dK = dV = 0; rows
+ * with no visible key (LSE = -inf) get dQ = 0 and contribute nothing.
+ * kv_lens must not overlap dQ, dK, dV or the workspace.
+ */
+fa_status fa_backward_masked(const void* Q, const void* K, const void* V,
+                             const void* O, const void* dO, const float* LSE,
+                             const int* kv_lens,
+                             void* dQ, void* dK, void* dV,
+                             void* workspace, size_t workspace_bytes,
+                             int B, int H, int Nq, int Nk, int D,
+                             float scale, int causal, hipStream_t stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa_status_string(fa_status s);

@@ -44,13 +44,13 @@ def g(n):
     return n * 2.0 ** -24
 
 
-def bounds_head(q, k, v, do, o_gpu, lse_err, scale, causal):
+def bounds_head(q, k, v, do, o_gpu, lse_err, scale, causal, kv_len=None):
     """Per-element error bounds (dQ, dK, dV) of one head, from the module
     docstring's derivation. Inputs are fp64 arrays of the bf16 values;
-    lse_err [Nq] is the forward's LSE error."""
+    lse_err [Nq] is the forward's LSE error (0 on rows with no key)."""
     nq, D = q.shape
     nk = k.shape[0]
-    p = orc.softmax_weights(q, k, scale, causal)
+    p = orc.softmax_weights(q, k, scale, causal, kv_len)
     eps = np.expm1(lse_err[:, None] + scale * g(D) * (np.abs(q) @ np.abs(k).T)) + 2.0 ** -16
     dp = do @ v.T
     d_exact = (p * dp).sum(axis=1, keepdims=True)

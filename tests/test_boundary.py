@@ -34,8 +34,9 @@ def declared_functions():
 
 def test_header_declares_the_api():
     assert declared_functions() == sorted(
-        ["fa_forward", "fa_forward_f32", "fa_decode_workspace_bytes", "fa_decode_splitkv",
-         "fa_backward_workspace_bytes", "fa_backward", "fa_status_string"])
+        ["fa_forward", "fa_forward_masked", "fa_forward_f32", "fa_forward_f32_masked",
+         "fa_decode_workspace_bytes", "fa_decode_splitkv", "fa_decode_splitkv_masked",
+         "fa_backward_workspace_bytes", "fa_backward", "fa_backward_masked", "fa_status_string"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -76,6 +77,23 @@ def test_forward_rejects_bad_arguments(lib, fn):
     assert fwd(lib, fn, O=FAKE) == INVALID                           # O aliases Q
     assert fwd(lib, fn, O=FAKE + 0x100000 + 64) == INVALID           # O overlaps K
     assert fwd(lib, fn, B=65536, H=65536, Nq=1024) == UNSUPPORTED    # grid too large
+    assert fwd(lib, fn, causal=3) == INVALID                          # no such alignment
+    assert fwd(lib, fn, causal=-1) == INVALID
+
+
+@pytest.mark.parametrize("fn", ["fa_forward_masked", "fa_forward_f32_masked"])
+def test_masked_forward_rejects_bad_kv_lens(lib, fn):
+    def call(lens, **kw):
+        a = dict(Q=FAKE, K=FAKE + 0x100000, V=FAKE + 0x200000, O=FAKE + 0x300000, L=None, B=2, H=1, Nq=16,
+                 Nk=16, D=64, scale=0.125, causal=2)
+        a.update(kw)
+        return getattr(lib, fn)(a["Q"], a["K"], a["V"], a["O"], a["L"], lens, a["B"], a["H"], a["Nq"], a["Nk"],
+                                a["D"], a["scale"], a["causal"], None)
+    assert call(FAKE + 0x400002) == INVALID                           # misaligned kv_lens
+    assert call(FAKE + 0x300000) == INVALID                           # kv_lens inside O
+    assert call(FAKE + 0x500000, L=FAKE + 0x500000) == INVALID        # kv_lens inside LSE
+    assert call(FAKE + 0x400000, causal=5) == INVALID
+    assert call(FAKE + 0x400000, B=0) == 0                            # nothing to do
 
 
 @pytest.mark.parametrize("fn", ["fa_forward", "fa_forward_f32"])
@@ -142,6 +160,7 @@ def test_backward_rejects_bad_arguments(lib):
     assert bwd(lib, dV=FAKE + 0x700000 + 64) == INVALID              # dV overlaps dK
     assert bwd(lib, W=FAKE + 0x600000) == INVALID                    # workspace overlaps dQ
     assert bwd(lib, B=65536, H=65536, Nq=1024) == UNSUPPORTED        # grid too large
+    assert bwd(lib, causal=3) == INVALID
     # nothing to compute: returns before any pointer is looked at
     none = dict(Q=None, K=None, V=None, O=None, dO=None, L=None, dQ=None, dK=None, dV=None, W=None)
     assert bwd(lib, B=0, **none) == 0
@@ -149,6 +168,28 @@ def test_backward_rejects_bad_arguments(lib):
     # Nq = 0 < Nk zeroes dK, dV: those two must be valid
     assert bwd(lib, Nq=0, dK=None) == INVALID
     assert bwd(lib, Nq=0, dV=FAKE + 0x700000) == INVALID             # dV aliases dK
+
+
+def test_masked_backward_and_decode_reject_bad_kv_lens(lib):
+    def bm(lens, **kw):
+        a = dict(Q=FAKE, K=FAKE + 0x100000, V=FAKE + 0x200000, O=FAKE + 0x300000, dO=FAKE + 0x400000,
+                 L=FAKE + 0x500000, dQ=FAKE + 0x600000, dK=FAKE + 0x700000, dV=FAKE + 0x800000, W=FAKE + 0x900000,
+                 B=2, H=2, Nq=100, Nk=100, D=128, scale=0.1, causal=2)
+        a.update(kw)
+        return lib.fa_backward_masked(a["Q"], a["K"], a["V"], a["O"], a["dO"], a["L"], lens, a["dQ"], a["dK"],
+                                      a["dV"], a["W"], a["B"] * a["H"] * a["Nq"] * 4, a["B"], a["H"], a["Nq"],
+                                      a["Nk"], a["D"], a["scale"], a["causal"], None)
+    assert bm(FAKE + 0xA00002) == INVALID                             # misaligned
+    assert bm(FAKE + 0x700000 + 16) == INVALID                        # inside dK
+    assert bm(FAKE + 0x900000) == INVALID                             # inside the workspace
+    assert bm(FAKE + 0xA00000, causal=4) == INVALID
+
+    def dm(lens, W=FAKE + 0x400000):
+        return lib.fa_decode_splitkv_masked(FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, None, lens,
+                                            W, 2 * 2 * 4 * 130 * 4, 2, 2, 100, 128, 0.1, 4, None)
+    assert dm(FAKE + 0x500002) == INVALID                             # misaligned
+    assert dm(FAKE + 0x400000 + 64) == INVALID                        # inside the workspace
+    assert dm(FAKE + 0x300000) == INVALID                             # inside O
 
 
 def test_python_binding_refuses_cpu_tensors(lib):
