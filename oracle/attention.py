@@ -22,6 +22,10 @@ Sources (the web pages the method is defined on):
   (m, l, O with alpha = exp(m - m_new), final O / l).
 * "Kernel visualization: Flash Attention 2", section "Write the data back to
   HBM" (L = m + log l written beside O).
+* phobos attention stdlib page, "Rotary position embeddings": ``rope``
+  (rotate-half form: halves a, b of a row become a cos - b sin, b cos + a sin)
+  and ``rope_pairs`` (adjacent pairs 2i, 2i + 1 rotated the same way); cos and
+  sin are [R, D / 2], the angles of each row's position.
 * phobos attention stdlib page, ``attention`` (mask of the ragged last key
   block) and ``Causal attention``.
 
@@ -40,6 +44,12 @@ What pins each function (tests/test_oracle.py):
 * ``merge`` / ``split_states`` / ``combine``: the numbers of the solution to
   exercise 3 (tests/golden/merge_example.json); every chunking of a row gives
   the two-pass answer.
+* ``rope`` / ``rope_pairs`` / ``attention_rope``: closed forms (zero angle is
+  the identity, a quarter turn maps (a, b) to (-b, a)), every pair keeps its
+  length, two rotations add their angles, the pairs form is the half form
+  under the interleaving permutation, and the score of a rotated query and
+  key depends only on the difference of their positions (shifting every
+  position leaves ``attention_rope`` unchanged).
 * ``attention_backward``: central finite differences of ``attention`` on tiny
   inputs; torch's float64 CPU autograd through ``scaled_dot_product_attention``
   as an independent library routine; closed forms (dO = 0 gives zero
@@ -310,6 +320,61 @@ def decode(q, k, v, scale: float, kv_lens=None):
     The same definition as ``attention`` with Nq = 1; returns O [B, H, 1, D]
     and LSE [B, H, 1]."""
     return attention(q, k, v, scale, causal=False, kv_lens=kv_lens)
+
+
+# --------------------------------------------------------------------------
+# Rotary position embeddings (phobos page, "Rotary position embeddings").
+# --------------------------------------------------------------------------
+
+def rope(x, cos, sin):
+    """Rotate-half RoPE of the rows of x [R, D]: with a = x[:, :D/2] and
+    b = x[:, D/2:], the row becomes [a cos - b sin, b cos + a sin]; cos and
+    sin are [R, D/2]. Both halves are read before either is written."""
+    x, cos, sin = _f64(x), _f64(cos), _f64(sin)
+    half = x.shape[1] // 2
+    a, b = x[:, :half], x[:, half:]
+    return np.concatenate([a * cos - b * sin, b * cos + a * sin], axis=1)
+
+
+def rope_pairs(x, cos, sin):
+    """Adjacent-pair RoPE (GPT-J form): elements x0 = x[:, 2i] and
+    x1 = x[:, 2i + 1] become x0 cos - x1 sin and x1 cos + x0 sin; cos and sin
+    are [R, D/2]."""
+    x, cos, sin = _f64(x), _f64(cos), _f64(sin)
+    x0, x1 = x[:, 0::2], x[:, 1::2]
+    out = np.empty_like(x)
+    out[:, 0::2] = x0 * cos - x1 * sin
+    out[:, 1::2] = x1 * cos + x0 * sin
+    return out
+
+
+ROPE_HALF, ROPE_PAIRS = 0, 1
+
+
+def attention_rope(q, k, v, cos, sin, scale: float, causal=False, kv_lens=None, style: int = ROPE_HALF):
+    """Attention of rotated queries and keys: softmax(rope(Q) rope(K)^T scale) V.
+
+    cos, sin: [P, D/2] tables indexed by position. Key j has position j. Query
+    row i has position i, or i + (Lk - Nq) under bottom-right causal alignment
+    (the queries are then the newest tokens); rows whose position would be
+    negative see no key and are not rotated. Returns (O, LSE) as ``attention``.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    cos, sin = _f64(cos), _f64(sin)
+    b, h, nq, d = q.shape
+    nk = k.shape[2]
+    rot = rope if style == ROPE_HALF else rope_pairs
+    qr = np.empty_like(q)
+    kr = np.empty_like(k)
+    for bi in range(b):
+        L = nk if kv_lens is None else int(kv_lens[bi])
+        qpos = np.arange(nq) + (L - nq if int(causal) == CAUSAL_BOTTOM_RIGHT else 0)
+        qpos = np.maximum(qpos, 0)
+        kpos = np.arange(nk)
+        for hi in range(h):
+            qr[bi, hi] = rot(q[bi, hi], cos[qpos], sin[qpos])
+            kr[bi, hi] = rot(k[bi, hi], cos[kpos], sin[kpos])
+    return attention(qr, kr, v, scale, causal, kv_lens)
 
 
 # --------------------------------------------------------------------------

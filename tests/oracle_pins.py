@@ -507,6 +507,64 @@ def pin_backward_masks(orc):
     _close(dv[0], tv.grad.numpy(), 1e-12, "masked autograd dV")
 
 
+# ---- rotary position embeddings ----------------------------------------------
+
+def _angles(pos, half, base=100.0):
+    return np.outer(pos, base ** (-np.arange(half) / half))
+
+
+def pin_rope_closed_forms(orc):
+    """Zero angle is the identity; a quarter turn maps the halves (a, b) to
+    (-b, a) (pairs: (x0, x1) to (-x1, x0)); every rotated pair keeps its
+    length; rotating by alpha then beta is rotating by alpha + beta; the pairs
+    form is the half form under the interleaving permutation."""
+    x = _rand((5, 8), 100)
+    one, zero = np.ones((5, 4)), np.zeros((5, 4))
+    _close(orc.rope(x, one, zero), x, 0.0, "rope identity")
+    _close(orc.rope_pairs(x, one, zero), x, 0.0, "rope_pairs identity")
+    _close(orc.rope(x, zero, one), np.concatenate([-x[:, 4:], x[:, :4]], axis=1), 0.0, "rope quarter turn")
+    quarter = np.empty_like(x)
+    quarter[:, 0::2], quarter[:, 1::2] = -x[:, 1::2], x[:, 0::2]
+    _close(orc.rope_pairs(x, zero, one), quarter, 0.0, "rope_pairs quarter turn")
+    th1, th2 = _rand((5, 4), 101), _rand((5, 4), 102)
+    y = orc.rope(x, np.cos(th1), np.sin(th1))
+    _close(np.hypot(y[:, :4], y[:, 4:]), np.hypot(x[:, :4], x[:, 4:]), 1e-14, "rope keeps pair lengths")
+    _close(orc.rope(y, np.cos(th2), np.sin(th2)), orc.rope(x, np.cos(th1 + th2), np.sin(th1 + th2)), 1e-14,
+           "rope angles add")
+    perm = np.concatenate([np.arange(0, 8, 2), np.arange(1, 8, 2)])   # pairs layout -> halves layout
+    z = orc.rope_pairs(x, np.cos(th1), np.sin(th1))
+    _close(z[:, perm], orc.rope(x[:, perm], np.cos(th1), np.sin(th1)), 1e-15, "pairs = half under interleaving")
+
+
+def pin_rope_relative_position(orc):
+    """With angles proportional to position, the score of a rotated query at
+    position m and key at n depends only on m - n: shifting every position by
+    the same amount leaves attention_rope unchanged (non-causal and top-left;
+    both styles)."""
+    nq, nk, d = 6, 9, 8
+    q = _rand((1, 2, nq, d), 103)
+    k = _rand((1, 2, nk, d), 104)
+    v = _rand((1, 2, nk, d), 105)
+    n_pos = 40
+    ang = _angles(np.arange(n_pos), d // 2)
+    cos, sin = np.cos(ang), np.sin(ang)
+    shift = 17
+    for style in (orc.ROPE_HALF, orc.ROPE_PAIRS):
+        for causal in (0, 1):
+            o, lse = orc.attention_rope(q, k, v, cos, sin, 0.4, causal, style=style)
+            o2, lse2 = orc.attention_rope(q, k, v, cos[shift:], sin[shift:], 0.4, causal, style=style)
+            _close(o, o2, 1e-12, f"rope shift invariance O style={style} causal={causal}")
+            _close(lse, lse2, 1e-12, f"rope shift invariance LSE style={style} causal={causal}")
+            o0, _ = orc.attention(q, k, v, 0.4, causal)
+            assert np.abs(o - o0).max() > 1e-3, "rotation must change the result"
+    # bottom-right: the queries are the newest tokens, so they take positions Nk - Nq + i
+    o_br, _ = orc.attention_rope(q, k, v, cos, sin, 0.4, 2)
+    qr = np.stack([orc.rope(q[0, hh], cos[nk - nq: nk], sin[nk - nq: nk]) for hh in range(2)])[None]
+    kr = np.stack([orc.rope(k[0, hh], cos[:nk], sin[:nk]) for hh in range(2)])[None]
+    o_ref, _ = orc.attention(qr, kr, v, 0.4, 2)
+    _close(o_br, o_ref, 1e-13, "rope bottom-right positions")
+
+
 ALL_PINS = [
     pin_worked_example_trace,
     pin_worked_example_two_pass,
@@ -532,4 +590,6 @@ ALL_PINS = [
     pin_online_blocked_masks,
     pin_decode_padding,
     pin_backward_masks,
+    pin_rope_closed_forms,
+    pin_rope_relative_position,
 ]

@@ -40,6 +40,12 @@ MUTATIONS = {
     "bwd_softmax_jacobian_sign": ("ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))",
                                   "ds = p * (dp + (p * dp).sum(axis=1, keepdims=True))"),
     "bwd_softmax_jacobian_dropped": ("ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))", "ds = p * dp"),
+    "rope_sign": ("return np.concatenate([a * cos - b * sin, b * cos + a * sin], axis=1)",
+                  "return np.concatenate([a * cos + b * sin, b * cos - a * sin], axis=1)"),
+    "rope_halves_swapped": ("a, b = x[:, :half], x[:, half:]", "b, a = x[:, :half], x[:, half:]"),
+    "rope_pairs_wrong_partner": ("out[:, 1::2] = x1 * cos + x0 * sin", "out[:, 1::2] = x1 * cos + x1 * sin"),
+    "rope_query_positions_top_left": ("qpos = np.arange(nq) + (L - nq if int(causal) == CAUSAL_BOTTOM_RIGHT else 0)",
+                                      "qpos = np.arange(nq)"),
     "bwd_dq_no_scale": ("dq = scale * (ds @ k)", "dq = ds @ k"),
     "bwd_dk_wrong_operand": ("dk = scale * (ds.T @ q)", "dk = scale * (ds.T @ k)"),
 }
