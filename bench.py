@@ -187,8 +187,8 @@ def main():
         files = ["fa_fwd_f32.hip", "fa_device.h", "fa_internal.h"]
     else:
         step = lambda: fa.fa_forward(q, k, v, causal=w.causal, scale=w.scale, out=out, lse=lse)  # noqa: E731
-        peak, dtype, kname = PEAK_BF16_TFLOPS, "bf16", "fwd_bf16_kernel"
-        files = ["fa_fwd_bf16.hip", "fa_device.h", "fa_internal.h"]
+        peak, dtype, kname = PEAK_BF16_TFLOPS, "bf16", "fwd_mfma_kernel"
+        files = ["fa_fwd_mfma.hip", "fa_device.h", "fa_internal.h"]
     ms = time_steps(step, args.steps, args.warmup, torch)
     flops, _ = workload_counts(w)
     tflops = flops / (ms * 1e-3) / 1e12

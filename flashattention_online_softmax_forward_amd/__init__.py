@@ -23,12 +23,20 @@ import torch
 from . import _lib
 
 CAUSAL_NONE, CAUSAL_TOP_LEFT, CAUSAL_BOTTOM_RIGHT = 0, 1, 2
+ROPE_HALF, ROPE_PAIRS = 0, 1
+_DTYPES = {torch.bfloat16: 0, torch.float16: 1}
 
 __all__ = [
     "CAUSAL_NONE",
     "CAUSAL_TOP_LEFT",
     "CAUSAL_BOTTOM_RIGHT",
     "fa_forward",
+    "fa_forward_f16",
+    "fa_forward_rope",
+    "fa_rope",
+    "fa_rope_workspace_bytes",
+    "ROPE_HALF",
+    "ROPE_PAIRS",
     "fa_forward_f32",
     "fa_decode_splitkv",
     "fa_decode_workspace_bytes",
@@ -127,6 +135,15 @@ def fa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal=False,
                ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """bf16 forward: returns (O bf16 [B,H,Nq,D], LSE fp32 [B,H,Nq] or None)."""
     return _forward("fa_forward", torch.bfloat16, q, k, v, causal, scale, out, lse, want_lse, kv_lens)
+
+
+def fa_forward_f16(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal=False,
+                   scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                   kv_lens: Optional[torch.Tensor] = None
+                   ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """fp16 forward: returns (O fp16 [B,H,Nq,D], LSE fp32 [B,H,Nq] or None)."""
+    return _forward("fa_forward_f16", torch.float16, q, k, v, causal, scale, out, lse, want_lse, kv_lens)
 
 
 def fa_forward_f32(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal=False,
@@ -241,3 +258,88 @@ def fa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tens
                                               mode, _stream(q))
     _lib.check(code, "fa_backward")
     return dq, dk, dv
+
+
+def _rope_style(style) -> int:
+    if isinstance(style, str):
+        names = {"half": ROPE_HALF, "pairs": ROPE_PAIRS}
+        if style not in names:
+            raise ValueError(f"style must be one of {sorted(names)} (got {style!r})")
+        return names[style]
+    if int(style) not in (ROPE_HALF, ROPE_PAIRS):
+        raise ValueError(f"style must be 0 (half) or 1 (pairs), got {style!r}")
+    return int(style)
+
+
+def _check_tables(cos, sin, D, device):
+    for name, t in (("cos", cos), ("sin", sin)):
+        _check_tensor(name, t, torch.float32, ndim=2)
+        if t.shape[1] != D // 2:
+            raise ValueError(f"{name} must be [n_pos, {D // 2}]")
+        if t.device != device:
+            raise ValueError(f"{name} must live on {device}")
+    if cos.shape != sin.shape:
+        raise ValueError("cos and sin must have the same shape")
+    return cos.shape[0]
+
+
+def fa_rope(x: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor, style="half",
+            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Rotary position embedding of x [B,H,N,D] (bf16 or fp16): row n rotated by
+    cos[n], sin[n] (fp32 [n_pos, D/2]). ``out`` may be ``x`` (in place)."""
+    if x.dtype not in _DTYPES:
+        raise TypeError(f"x must be bfloat16 or float16 (got {x.dtype})")
+    _check_tensor("x", x, x.dtype)
+    B, H, N, D = x.shape
+    n_pos = _check_tables(cos, sin, D, x.device)
+    out = torch.empty_like(x) if out is None else out
+    _check_tensor("out", out, x.dtype)
+    if out.shape != x.shape:
+        raise ValueError("out must have x's shape")
+    code = _lib.load().fa_rope(x.data_ptr(), out.data_ptr(), cos.data_ptr(), sin.data_ptr(), n_pos,
+                               _rope_style(style), _DTYPES[x.dtype], B, H, N, D, _stream(x))
+    _lib.check(code, "fa_rope")
+    return out
+
+
+def fa_rope_workspace_bytes(B: int, H: int, Nk: int, D: int) -> int:
+    return int(_lib.load().fa_rope_workspace_bytes(B, H, Nk, D))
+
+
+def fa_forward_rope(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor,
+                    style="half", causal=False, scale: Optional[float] = None,
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    want_lse: bool = True, kv_lens: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None
+                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Forward pass of rope(Q), rope(K), V (bf16 or fp16): key j at position j,
+    query i at position i (i + Lk - Nq under bottom-right alignment).
+    Returns (O [B,H,Nq,D] in the input type, LSE fp32 [B,H,Nq] or None)."""
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"q must be bfloat16 or float16 (got {q.dtype})")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, q.dtype)
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    if tuple(k.shape) != (B, H, Nk, D) or tuple(v.shape) != (B, H, Nk, D):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    n_pos = _check_tables(cos, sin, D, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out = torch.empty_like(q) if out is None else out
+    _check_tensor("out", out, q.dtype)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_tensor("lse", lse, torch.float32, ndim=3)
+    need = fa_rope_workspace_bytes(B, H, Nk, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    kv_lens = _check_kv_lens(kv_lens, B, q.device)
+    code = _lib.load().fa_forward_rope(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr() if lse is not None else None,
+        kv_lens.data_ptr() if kv_lens is not None else None, cos.data_ptr(), sin.data_ptr(), n_pos,
+        _rope_style(style), _DTYPES[q.dtype], workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        B, H, Nq, Nk, D, float(scale), _causal_mode(causal), _stream(q))
+    _lib.check(code, "fa_forward_rope")
+    return out, lse

@@ -9,6 +9,8 @@
 #include "fa.h"
 #include "fa_internal.h"
 
+static_assert(FA_ROPE_HALF == fa::kRopeHalf && FA_ROPE_PAIRS == fa::kRopePairs,
+              "RoPE styles of the C ABI and the kernels agree");
 static_assert(FA_CAUSAL_NONE == fa::kCausalNone && FA_CAUSAL_TOP_LEFT == fa::kCausalTopLeft &&
                   FA_CAUSAL_BOTTOM_RIGHT == fa::kCausalBottomRight,
               "causal modes of the C ABI and the kernels agree");
@@ -94,6 +96,86 @@ fa_status fa_forward_masked(const void* Q, const void* K, const void* V, void* O
 fa_status fa_forward(const void* Q, const void* K, const void* V, void* O, float* LSE,
                      int B, int H, int Nq, int Nk, int D, float scale, int causal, hipStream_t stream) {
     return fa_forward_masked(Q, K, V, O, LSE, nullptr, B, H, Nq, Nk, D, scale, causal, stream);
+}
+
+fa_status fa_forward_f16_masked(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                                const int* kv_lens, int B, int H, int Nq, int Nk, int D, float scale, int causal,
+                                hipStream_t stream) {
+    if (!good_causal(causal)) return FA_ERR_INVALID_ARG;
+    bool nothing = false;
+    const fa_status st = check_forward(Q, K, V, O, LSE, B, H, Nq, Nk, D, scale, 2, fa::BM_FWD, &nothing);
+    if (st != FA_OK || nothing) return st;
+    if (!good_kv_lens(kv_lens, B, O, (size_t)B * H * Nq * D * 2, LSE, (size_t)B * H * Nq * 4))
+        return FA_ERR_INVALID_ARG;
+    const fa::FwdArgs a{Q, K, V, O, LSE, kv_lens, B, H, Nq, Nk, D, scale, causal, stream};
+    return fa::launch_fwd_f16(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+fa_status fa_forward_f16(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                         int B, int H, int Nq, int Nk, int D, float scale, int causal, hipStream_t stream) {
+    return fa_forward_f16_masked(Q, K, V, O, LSE, nullptr, B, H, Nq, Nk, D, scale, causal, stream);
+}
+
+size_t fa_rope_workspace_bytes(int B, int H, int Nk, int D) {
+    if (B < 0 || H < 0 || Nk < 0 || (D != 64 && D != 128)) return 0;
+    return (size_t)B * H * Nk * D * 2;
+}
+
+fa_status fa_rope(const void* X, void* Y, const float* cos_t, const float* sin_t, int n_pos, int style,
+                  int dtype, int B, int H, int N, int D, hipStream_t stream) {
+    if (B < 0 || H < 0 || N < 0 || n_pos < 0) return FA_ERR_INVALID_ARG;
+    if (style != FA_ROPE_HALF && style != FA_ROPE_PAIRS) return FA_ERR_INVALID_ARG;
+    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_INVALID_ARG;
+    if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * H * N == 0) return FA_OK;
+    if (n_pos < N) return FA_ERR_INVALID_ARG;
+    if (!X || !Y || !cos_t || !sin_t) return FA_ERR_INVALID_ARG;
+    if (!aligned16(X) || !aligned16(Y) || !aligned16(cos_t) || !aligned16(sin_t)) return FA_ERR_INVALID_ARG;
+    const size_t bytes = (size_t)B * H * N * D * 2, tab = (size_t)n_pos * (D / 2) * sizeof(float);
+    // In place (Y == X) is allowed; a partial overlap is not.
+    if (Y != X && overlaps(X, bytes, Y, bytes)) return FA_ERR_INVALID_ARG;
+    if (overlaps(Y, bytes, cos_t, tab) || overlaps(Y, bytes, sin_t, tab)) return FA_ERR_INVALID_ARG;
+    if ((long long)B * H * N / (256 / (D / 16)) + 1 > INT_MAX) return FA_ERR_UNSUPPORTED;
+    const fa::RopeArgs a{X, Y, cos_t, sin_t, B, H, N, D, style, dtype == FA_DTYPE_F16, stream};
+    return fa::launch_rope(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+fa_status fa_forward_rope(const void* Q, const void* K, const void* V, void* O, float* LSE, const int* kv_lens,
+                          const float* cos_t, const float* sin_t, int n_pos, int style, int dtype,
+                          void* workspace, size_t workspace_bytes, int B, int H, int Nq, int Nk, int D,
+                          float scale, int causal, hipStream_t stream) {
+    if (!good_causal(causal)) return FA_ERR_INVALID_ARG;
+    if (style != FA_ROPE_HALF && style != FA_ROPE_PAIRS) return FA_ERR_INVALID_ARG;
+    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_INVALID_ARG;
+    bool nothing = false;
+    const fa_status st = check_forward(Q, K, V, O, LSE, B, H, Nq, Nk, D, scale, 2, fa::BM_FWD, &nothing);
+    if (st != FA_OK || nothing) return st;
+    const size_t bq = (size_t)B * H * Nq * D * 2, bkv = (size_t)B * H * Nk * D * 2;
+    const size_t bl = (size_t)B * H * Nq * 4, tab = (size_t)n_pos * (D / 2) * sizeof(float);
+    if (!good_kv_lens(kv_lens, B, O, bq, LSE, bl)) return FA_ERR_INVALID_ARG;
+    if (n_pos < Nq || n_pos < Nk || !cos_t || !sin_t || !aligned16(cos_t) || !aligned16(sin_t))
+        return FA_ERR_INVALID_ARG;
+    const size_t need = fa_rope_workspace_bytes(B, H, Nk, D);
+    if (!workspace || !aligned16(workspace) || workspace_bytes < need) return FA_ERR_INVALID_ARG;
+    const void* ins[5] = {Q, K, V, cos_t, sin_t};
+    const size_t in_bytes[5] = {bq, bkv, bkv, tab, tab};
+    for (int j = 0; j < 5; ++j)
+        if (overlaps(workspace, need, ins[j], in_bytes[j]) || overlaps(O, bq, ins[j], in_bytes[j]))
+            return FA_ERR_INVALID_ARG;
+    if (overlaps(workspace, need, O, bq) || overlaps(workspace, need, LSE, bl) ||
+        overlaps(workspace, need, kv_lens, (size_t)B * 4))
+        return FA_ERR_INVALID_ARG;
+    if ((long long)B * H * Nk / (256 / (D / 16)) + 1 > INT_MAX) return FA_ERR_UNSUPPORTED;
+    // K rotated once into the workspace (positions 0..Nk-1), then the
+    // attention kernel rotates Q in registers and reads the rotated K.
+    const fa::RopeArgs r{K, workspace, cos_t, sin_t, B, H, Nk, D, style, dtype == FA_DTYPE_F16, stream};
+    if (fa::launch_rope(r) != hipSuccess) return FA_ERR_LAUNCH;
+    fa::FwdArgs a{Q, workspace, V, O, LSE, kv_lens, B, H, Nq, Nk, D, scale, causal, stream};
+    a.rope_cos = cos_t;
+    a.rope_sin = sin_t;
+    a.rope_style = style;
+    const hipError_t e = dtype == FA_DTYPE_F16 ? fa::launch_fwd_f16(a) : fa::launch_fwd_bf16(a);
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 fa_status fa_forward_f32_masked(const float* Q, const float* K, const float* V, float* O, float* LSE,

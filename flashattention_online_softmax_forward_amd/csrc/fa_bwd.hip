@@ -48,7 +48,7 @@ constexpr int kBT = 32;                    // rows per streamed tile
 static_assert(BM_BWD == 32 * kBwdWaves, "32 rows per wave");
 
 #define LDS_AS __attribute__((address_space(3)))
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
 
 // Lane-row i of an MFMA A operand reads tile row perm(i) (bits 2 and 3
 // swapped): accumulator register r of lane (j, h) then holds row

@@ -31,6 +31,84 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+// The fp16 MFMA and transpose-read builtins take __fp16 vectors.
+typedef __fp16 fp16x8_t __attribute__((ext_vector_type(8)));
+typedef __fp16 fp16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+// Low / high fp16 of a packed word widened to fp32 (exact).
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+    return (float)__builtin_bit_cast(f16x2_t, w)[0];
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+    return (float)__builtin_bit_cast(f16x2_t, w)[1];
+}
+
+// The 16-bit input types the MFMA kernels are instantiated for (bf16 and
+// fp16): operand vectors, the 32x32x16 MFMA with fp32 accumulation, the LDS
+// transpose read, round-to-nearest-even packing of two fp32 values, and
+// widening of the halves of a packed word.
+template <typename T> struct Elem;
+template <> struct Elem<__bf16> {
+    using v8 = bf16x8_t;
+    using v4 = bf16x4_t;
+    __device__ static __forceinline__ f32x16_t mfma(v8 a, v8 b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ v4 tr_read(__attribute__((address_space(3))) v4* p) {
+        return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p);
+    }
+    __device__ static __forceinline__ uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
+    __device__ static __forceinline__ float lo(uint32_t w) { return bf16_lo(w); }
+    __device__ static __forceinline__ float hi(uint32_t w) { return bf16_hi(w); }
+};
+template <> struct Elem<_Float16> {
+    using v8 = fp16x8_t;
+    using v4 = fp16x4_t;
+    __device__ static __forceinline__ f32x16_t mfma(v8 a, v8 b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ v4 tr_read(__attribute__((address_space(3))) v4* p) {
+        return __builtin_amdgcn_ds_read_tr16_b64_v4f16(p);
+    }
+    __device__ static __forceinline__ uint32_t pack2(float lo, float hi) {
+        f16x2_t v = {(_Float16)lo, (_Float16)hi};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+    __device__ static __forceinline__ float lo(uint32_t w) { return f16_lo(w); }
+    __device__ static __forceinline__ float hi(uint32_t w) { return f16_hi(w); }
+};
+
+// Rotary position embedding of 16-byte chunks (8 elements of type T), in
+// fp32 and rounded back to T (phobos page, "Rotary position embeddings").
+//   rotate-half: chunk `a` holds elements i..i+7 of the first half of a row
+//   and `b` the same elements of the second half; with c = cos[i..i+7] and
+//   s = sin[i..i+7], a <- a c - b s and b <- b c + a s.
+//   adjacent pairs: chunk `w` holds elements 2p..2p+7, i.e. pairs p..p+3;
+//   with c = cos[p..p+3], s = sin[p..p+3], (x0, x1) <- (x0 c - x1 s, x1 c + x0 s).
+template <typename T>
+__device__ __forceinline__ void rope_half_chunks(uint32_t* a, uint32_t* b, const float* c, const float* s) {
+    using E = Elem<T>;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const float a0 = E::lo(a[w]), a1 = E::hi(a[w]), b0 = E::lo(b[w]), b1 = E::hi(b[w]);
+        const float c0 = c[2 * w], c1 = c[2 * w + 1], s0 = s[2 * w], s1 = s[2 * w + 1];
+        a[w] = E::pack2(__builtin_fmaf(a0, c0, -b0 * s0), __builtin_fmaf(a1, c1, -b1 * s1));
+        b[w] = E::pack2(__builtin_fmaf(b0, c0, a0 * s0), __builtin_fmaf(b1, c1, a1 * s1));
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void rope_pair_chunk(uint32_t* x, const float* c, const float* s) {
+    using E = Elem<T>;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const float x0 = E::lo(x[w]), x1 = E::hi(x[w]);
+        x[w] = E::pack2(__builtin_fmaf(x0, c[w], -x1 * s[w]), __builtin_fmaf(x1, c[w], x0 * s[w]));
+    }
+}
+
 // Hardware base-2 exponential (v_exp_f32); exp2(-inf) = 0.
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -1,4 +1,7 @@
-// bf16 FlashAttention forward for gfx950: MFMA for both contractions.
+// FlashAttention forward for gfx950 with bf16 or fp16 inputs: MFMA for both
+// contractions (v_mfma_f32_32x32x16_bf16 / _f16, fp32 accumulation). The two
+// input types share every line below; Elem<T> supplies the MFMA, the LDS
+// transpose read and the round-to-nearest-even packing of P and O.
 //
 // Method (iThome FlashAttention article, "three states"; ML compiler page,
 // section 11.9): a workgroup owns BM = 256 query rows of one (batch, head) and
@@ -93,17 +96,20 @@ __device__ __forceinline__ int v_swz(int key) {
 }
 
 #define LDS_AS __attribute__((address_space(3)))
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
-template <int D>
+template <typename T, int D>
 __global__ __launch_bounds__(kFwdThreads, 1)
-void fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
+void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                      const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
                      float* __restrict__ LSEg, const int* __restrict__ kv_lens, int H, int Nq, int Nk,
-                     int nqb, float scale2, int causal) {
+                     int nqb, float scale2, int causal, const float* __restrict__ rope_cos,
+                     const float* __restrict__ rope_sin, int rope_style) {
     // The causal mode is a uniform run-time argument rather than a template
     // parameter: one code shape for all keeps register allocation stable.
     const bool CAUSAL = causal != kCausalNone;
+    using E = Elem<T>;
+    using V8 = typename E::v8;
+    using V4 = typename E::v4;
     constexpr int BN = Bf16Tile<D>::BN;
     constexpr int TILE = BN * D;               // elements of one K (or V) tile
     constexpr int NCB = BN / 32;               // 32-key blocks of S^T
@@ -148,13 +154,51 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     const int qrow = wrow0 + j;
 
     // Q as the B operand: lane (j, h) holds row qrow, d = 16*kk + 8*h .. +7.
-    bf16x8_t qf[NKK];
+    u32x4_t qw[NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-        u32x4_t w = {0u, 0u, 0u, 0u};
-        if (qrow < Nq) w = *(const u32x4_t*)(Q + (size_t)qrow * D + kk * 16 + h * 8);
-        qf[kk] = __builtin_bit_cast(bf16x8_t, w);
+        qw[kk] = u32x4_t{0u, 0u, 0u, 0u};
+        if (qrow < Nq) qw[kk] = *(const u32x4_t*)(Q + (size_t)qrow * D + kk * 16 + h * 8);
     }
+    // Fused RoPE prologue on Q: the row is rotated in registers, once per
+    // workgroup, at its position (qrow, shifted by the bottom-right offset so
+    // the queries are the newest tokens). Both partners of every rotated pair
+    // are in this lane: d and d + D/2 (rotate-half) are chunks kk and
+    // kk + D/32 of the same half h; adjacent pairs share a chunk.
+    if (rope_cos && qrow < Nq) {
+        const int pos = max(0, qrow + off);
+        const float* cr = rope_cos + (size_t)pos * (D / 2);
+        const float* sr = rope_sin + (size_t)pos * (D / 2);
+        if (rope_style == kRopeHalf) {
+#pragma unroll
+            for (int kk = 0; kk < NKK / 2; ++kk) {
+                const int i0 = kk * 16 + h * 8;
+                const f32x4_t c0 = *(const f32x4_t*)(cr + i0), c1 = *(const f32x4_t*)(cr + i0 + 4);
+                const f32x4_t s0 = *(const f32x4_t*)(sr + i0), s1 = *(const f32x4_t*)(sr + i0 + 4);
+                const float c[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+                const float sn[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+                uint32_t a[4] = {qw[kk][0], qw[kk][1], qw[kk][2], qw[kk][3]};
+                uint32_t b[4] = {qw[kk + NKK / 2][0], qw[kk + NKK / 2][1], qw[kk + NKK / 2][2], qw[kk + NKK / 2][3]};
+                rope_half_chunks<T>(a, b, c, sn);
+                qw[kk] = u32x4_t{a[0], a[1], a[2], a[3]};
+                qw[kk + NKK / 2] = u32x4_t{b[0], b[1], b[2], b[3]};
+            }
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                const int p0 = kk * 8 + h * 4;
+                const f32x4_t c4 = *(const f32x4_t*)(cr + p0), s4 = *(const f32x4_t*)(sr + p0);
+                const float c[4] = {c4[0], c4[1], c4[2], c4[3]};
+                const float sn[4] = {s4[0], s4[1], s4[2], s4[3]};
+                uint32_t x[4] = {qw[kk][0], qw[kk][1], qw[kk][2], qw[kk][3]};
+                rope_pair_chunk<T>(x, c, sn);
+                qw[kk] = u32x4_t{x[0], x[1], x[2], x[3]};
+            }
+        }
+    }
+    V8 qf[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) qf[kk] = __builtin_bit_cast(V8, qw[kk]);
 
     int kend = Lk;
     if (CAUSAL) kend = max(0, min(Lk, min(q0 + BM_FWD, Nq) + off));
@@ -193,7 +237,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc_o[db][r] = 0.f;
     f32x16_t s[NCB];            // S^T of the tile between its MFMA step and its softmax step
-    bf16x8_t pf[NPV];           // P of the tile between its softmax step and its PV step
+    V8 pf[NPV];           // P of the tile between its softmax step and its PV step
 
     // Base-2 scaled maximum the row is accumulated against; kNoKeyMax until the
     // row's first visible key (finite, so masked scores give exp2(-inf) = 0).
@@ -214,22 +258,22 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     constexpr int LEAD = 4;                    // MFMAs of operand prefetch
     auto pv_operand = [&](const uint16_t* vb_prev, int i) __attribute__((always_inline)) {
         const int tt = i / NDB, db = i % NDB;
-        bf16x4_t part[2];
+        V4 part[2];
 #pragma unroll
         for (int rd = 0; rd < 2; ++rd) {
             const int key = tt * 16 + h * 8 + rd * 4 + (v_s >> 2);
             const int col = db * 32 + vb_blk * 16 + (v_s & 3) * 4;
             const int chunk = (col >> 3) ^ v_swz<CPR>(key);
             const uint16_t* addr = vb_prev + key * D + chunk * 8 + (col & 7);
-            part[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t*)(LDS_AS uint16_t*)addr);
+            part[rd] = E::tr_read((LDS_AS V4*)(LDS_AS uint16_t*)addr);
         }
-        return bf16x8_t{part[0][0], part[0][1], part[0][2], part[0][3],
+        return V8{part[0][0], part[0][1], part[0][2], part[0][3],
                         part[1][0], part[1][1], part[1][2], part[1][3]};
     };
     auto qk_operand = [&](const uint16_t* kb, int i) __attribute__((always_inline)) {
         const int kk = i / NCB, c = i % NCB;
         const int row = c * 32 + srow;
-        return *(const bf16x8_t*)(kb + row * D + (((kk * 2 + h) ^ k_swz<CPR>(row)) * 8));
+        return *(const V8*)(kb + row * D + (((kk * 2 + h) ^ k_swz<CPR>(row)) * 8));
     };
     auto step_mfma = [&](int t, const uint16_t* kb, const uint16_t* vb_prev) __attribute__((always_inline)) {
         __builtin_amdgcn_s_setprio(1);
@@ -243,19 +287,19 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
                 return i < NPVM ? pv_operand(vb_prev, i) : qk_operand(kb, i - NPVM);
             };
             const f32x16_t zero = {};
-            bf16x8_t ring[LEAD];
+            V8 ring[LEAD];
 #pragma unroll
             for (int i = 0; i < LEAD; ++i) ring[i] = operand(i);
             __builtin_amdgcn_sched_group_barrier(0x100, 2 * LEAD, 0);
 #pragma unroll
             for (int i = 0; i < NM; ++i) {
-                const bf16x8_t a = ring[i % LEAD];
+                const V8 a = ring[i % LEAD];
                 if (i + LEAD < NM) ring[i % LEAD] = operand(i + LEAD);
                 if (i < NPVM)
-                    acc_o[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[i / NDB], acc_o[i % NDB], 0, 0, 0);
+                    acc_o[i % NDB] = E::mfma(a, pf[i / NDB], acc_o[i % NDB]);
                 else  // the first d step of each key block starts from zero
-                    s[(i - NPVM) % NCB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        a, qf[(i - NPVM) / NCB], (i - NPVM) < NCB ? zero : s[(i - NPVM) % NCB], 0, 0, 0);
+                    s[(i - NPVM) % NCB] = E::mfma(
+                        a, qf[(i - NPVM) / NCB], (i - NPVM) < NCB ? zero : s[(i - NPVM) % NCB]);
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 const int nx = i + LEAD;
                 if (nx < NPVM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
@@ -264,14 +308,14 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
         } else if (do_pv) {
 #pragma unroll
             for (int i = 0; i < NPVM; ++i)
-                acc_o[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv_operand(vb_prev, i), pf[i / NDB],
-                                                                         acc_o[i % NDB], 0, 0, 0);
+                acc_o[i % NDB] = E::mfma(pv_operand(vb_prev, i), pf[i / NDB],
+                                                                         acc_o[i % NDB]);
         } else if (do_qk) {
             const f32x16_t zero = {};
 #pragma unroll
             for (int i = 0; i < NSM; ++i)
-                s[i % NCB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qk_operand(kb, i), qf[i / NCB],
-                                                                     i < NCB ? zero : s[i % NCB], 0, 0, 0);
+                s[i % NCB] = E::mfma(qk_operand(kb, i), qf[i / NCB],
+                                                                     i < NCB ? zero : s[i % NCB]);
         }
         __builtin_amdgcn_s_setprio(0);
     };
@@ -328,11 +372,11 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
                     lsc[e % NCH] += p[e];
                 }
                 u32x4_t w;
-                w[0] = pack_bf16x2(p[0], p[1]);
-                w[1] = pack_bf16x2(p[2], p[3]);
-                w[2] = pack_bf16x2(p[4], p[5]);
-                w[3] = pack_bf16x2(p[6], p[7]);
-                pf[c * 2 + u] = __builtin_bit_cast(bf16x8_t, w);
+                w[0] = E::pack2(p[0], p[1]);
+                w[1] = E::pack2(p[2], p[3]);
+                w[2] = E::pack2(p[4], p[5]);
+                w[3] = E::pack2(p[6], p[7]);
+                pf[c * 2 + u] = __builtin_bit_cast(V8, w);
             }
         const float lsum = (lsc[0] + lsc[1]) + (lsc[2] + lsc[3]);
         l_run += lsum;
@@ -404,8 +448,8 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
             for (int a4 = 0; a4 < 4; ++a4) {
                 const int d = db * 32 + a4 * 8 + h * 4;
                 u32x2_t w;
-                w[0] = pack_bf16x2(acc_o[db][a4 * 4 + 0] * inv, acc_o[db][a4 * 4 + 1] * inv);
-                w[1] = pack_bf16x2(acc_o[db][a4 * 4 + 2] * inv, acc_o[db][a4 * 4 + 3] * inv);
+                w[0] = E::pack2(acc_o[db][a4 * 4 + 0] * inv, acc_o[db][a4 * 4 + 1] * inv);
+                w[1] = E::pack2(acc_o[db][a4 * 4 + 2] * inv, acc_o[db][a4 * 4 + 3] * inv);
                 *(u32x2_t*)(orow + d) = w;
             }
         if (h == 0 && LSEg)
@@ -413,18 +457,23 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     }
 }
 
-template <int D>
+template <typename T, int D>
 static hipError_t launch_one(const FwdArgs& a) {
     const int nqb = (a.Nq + BM_FWD - 1) / BM_FWD;
     const int grid = a.B * a.H * nqb;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D>), dim3(grid), dim3(kFwdThreads), 0, a.stream,
+    hipLaunchKernelGGL((fwd_mfma_kernel<T, D>), dim3(grid), dim3(kFwdThreads), 0, a.stream,
                        (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
-                       (uint16_t*)a.O, a.LSE, a.kv_lens, a.H, a.Nq, a.Nk, nqb, a.scale * kLog2e, a.causal);
+                       (uint16_t*)a.O, a.LSE, a.kv_lens, a.H, a.Nq, a.Nk, nqb, a.scale * kLog2e, a.causal,
+                       a.rope_cos, a.rope_sin, a.rope_style);
     return hipGetLastError();
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
-    return a.D == 128 ? launch_one<128>(a) : launch_one<64>(a);
+    return a.D == 128 ? launch_one<__bf16, 128>(a) : launch_one<__bf16, 64>(a);
+}
+
+hipError_t launch_fwd_f16(const FwdArgs& a) {
+    return a.D == 128 ? launch_one<_Float16, 128>(a) : launch_one<_Float16, 64>(a);
 }
 
 }  // namespace fa

@@ -16,6 +16,10 @@ constexpr int kCausalNone = 0;
 constexpr int kCausalTopLeft = 1;
 constexpr int kCausalBottomRight = 2;
 
+// RoPE forms: rotate-half (halves a, b of a row) and adjacent pairs.
+constexpr int kRopeHalf = 0;
+constexpr int kRopePairs = 1;
+
 // Real key count of batch entry b: kv_lens[b] clamped to [0, Nk], or Nk.
 __device__ __forceinline__ int real_keys(const int* kv_lens, int b, int Nk) {
     return kv_lens ? min(max(kv_lens[b], 0), Nk) : Nk;
@@ -31,6 +35,22 @@ struct FwdArgs {
     int B, H, Nq, Nk, D;
     float scale;
     int causal;           // kCausalNone / kCausalTopLeft / kCausalBottomRight
+    hipStream_t stream;
+    // Fused RoPE on Q (bf16/fp16 MFMA forward only): cos/sin [n_pos, D/2] fp32,
+    // or NULL for none; K is expected already rotated.
+    const float* rope_cos = nullptr;
+    const float* rope_sin = nullptr;
+    int rope_style = 0;   // kRopeHalf / kRopePairs
+};
+
+struct RopeArgs {
+    const void* X;
+    void* Y;
+    const float* cos;
+    const float* sin;
+    int B, H, N, D;
+    int style;            // kRopeHalf / kRopePairs
+    bool f16;             // element type: fp16 (else bf16)
     hipStream_t stream;
 };
 
@@ -67,6 +87,8 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a);
+hipError_t launch_fwd_f16(const FwdArgs& a);
+hipError_t launch_rope(const RopeArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);

@@ -70,6 +70,21 @@ typedef enum fa_causal {
     FA_CAUSAL_BOTTOM_RIGHT = 2
 } fa_causal;
 
+/* Element type of the 16-bit entry points that take one (fa_rope, fa_forward_rope). */
+typedef enum fa_dtype {
+    FA_DTYPE_BF16 = 0,
+    FA_DTYPE_F16 = 1
+} fa_dtype;
+
+/* RoPE forms of the phobos page ("Rotary position embeddings"): rope, the
+ * rotate-half form of GPT-NeoX / LLaMA (halves a, b of a row become
+ * a cos - b sin, b cos + a sin), and rope_pairs, GPT-J's adjacent pairs
+ * (x[2i], x[2i+1]) rotated the same way by angle i. */
+typedef enum fa_rope_style {
+    FA_ROPE_HALF = 0,
+    FA_ROPE_PAIRS = 1
+} fa_rope_style;
+
 typedef enum fa_status {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad size, bad scale, workspace too small */
@@ -96,6 +111,60 @@ fa_status fa_forward_masked(const void* Q, const void* K, const void* V,
                             void* O, float* LSE, const int* kv_lens,
                             int B, int H, int Nq, int Nk, int D,
                             float scale, int causal, hipStream_t stream);
+
+/*
+ * The same operation with IEEE fp16 inputs and output (the f16 tensors of
+ * phobos' flash_attention kernel): fp16 MFMA with fp32 accumulation, P rounded
+ * to fp16 (round to nearest even) before the PV product, O rounded to fp16.
+ * Arguments as fa_forward / fa_forward_masked.
+ */
+fa_status fa_forward_f16(const void* Q, const void* K, const void* V,
+                         void* O, float* LSE,
+                         int B, int H, int Nq, int Nk, int D,
+                         float scale, int causal, hipStream_t stream);
+fa_status fa_forward_f16_masked(const void* Q, const void* K, const void* V,
+                                void* O, float* LSE, const int* kv_lens,
+                                int B, int H, int Nq, int Nk, int D,
+                                float scale, int causal, hipStream_t stream);
+
+/*
+ * Rotary position embedding of every row of X [B,H,N,D] (bf16 or fp16 per
+ * dtype) into Y: row n of each (b, h) is rotated by the angles of position n,
+ * cos[n, :] and sin[n, :] (fp32 [n_pos, D/2] tables, n_pos >= N, 16-byte
+ * aligned), in the given style. fp32 arithmetic, result rounded to the
+ * element type (nearest even). Y == X (in place) is allowed; any other
+ * overlap is not.
+ */
+fa_status fa_rope(const void* X, void* Y, const float* cos, const float* sin,
+                  int n_pos, int style, int dtype,
+                  int B, int H, int N, int D, hipStream_t stream);
+
+/* Bytes of workspace fa_forward_rope needs: B*H*Nk*D*2 (the rotated K). */
+size_t fa_rope_workspace_bytes(int B, int H, int Nk, int D);
+
+/*
+ * Forward pass with a fused RoPE prologue: O = softmax(rope(Q) rope(K)^T *
+ * scale) V (phobos page, "Rotary position embeddings", applied to the Q and K
+ * of its flash_attention). Key j has position j; query row i has position i,
+ * or i + (Lk - Nq) with FA_CAUSAL_BOTTOM_RIGHT (the queries are the newest
+ * tokens), clamped at 0 for rows that see no key. Q is rotated in registers
+ * inside the attention kernel; K is rotated once into `workspace` by the RoPE
+ * kernel (every K tile is read by every query block of its head, so rotating
+ * it in the key loop would repeat the work) and read from there. The rotated
+ * Q and K are rounded to the element type before the score product, as a
+ * separate RoPE pass writing that type would.
+ *   Q, K, V, O: dtype [B,H,N,D] as fa_forward / fa_forward_f16; LSE, kv_lens,
+ *   causal as fa_forward_masked; cos, sin: fp32 [n_pos, D/2], n_pos >= Nq and
+ *   >= Nk; workspace: >= fa_rope_workspace_bytes(B,H,Nk,D) bytes of device
+ *   memory, contents undefined on return, not shared by calls that overlap in
+ *   time. Two kernels run on `stream`.
+ */
+fa_status fa_forward_rope(const void* Q, const void* K, const void* V,
+                          void* O, float* LSE, const int* kv_lens,
+                          const float* cos, const float* sin, int n_pos, int style, int dtype,
+                          void* workspace, size_t workspace_bytes,
+                          int B, int H, int Nq, int Nk, int D,
+                          float scale, int causal, hipStream_t stream);
 
 /*
  * The same operation in fp32 end to end (fp32 inputs, fp32 arithmetic, fp32

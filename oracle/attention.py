@@ -351,15 +351,12 @@ def rope_pairs(x, cos, sin):
 ROPE_HALF, ROPE_PAIRS = 0, 1
 
 
-def attention_rope(q, k, v, cos, sin, scale: float, causal=False, kv_lens=None, style: int = ROPE_HALF):
-    """Attention of rotated queries and keys: softmax(rope(Q) rope(K)^T scale) V.
-
-    cos, sin: [P, D/2] tables indexed by position. Key j has position j. Query
-    row i has position i, or i + (Lk - Nq) under bottom-right causal alignment
-    (the queries are then the newest tokens); rows whose position would be
-    negative see no key and are not rotated. Returns (O, LSE) as ``attention``.
-    """
-    q, k, v = _f64(q), _f64(k), _f64(v)
+def rope_qk(q, k, cos, sin, causal=False, kv_lens=None, style: int = ROPE_HALF):
+    """rope(Q) and rope(K) of [B, H, N, D] tensors with the positions of
+    ``attention_rope``: key j at position j; query row i at position i, or
+    i + (Lk - Nq) under bottom-right causal alignment (the queries are then the
+    newest tokens), clamped at 0 (such rows see no key)."""
+    q, k = _f64(q), _f64(k)
     cos, sin = _f64(cos), _f64(sin)
     b, h, nq, d = q.shape
     nk = k.shape[2]
@@ -374,6 +371,16 @@ def attention_rope(q, k, v, cos, sin, scale: float, causal=False, kv_lens=None, 
         for hi in range(h):
             qr[bi, hi] = rot(q[bi, hi], cos[qpos], sin[qpos])
             kr[bi, hi] = rot(k[bi, hi], cos[kpos], sin[kpos])
+    return qr, kr
+
+
+def attention_rope(q, k, v, cos, sin, scale: float, causal=False, kv_lens=None, style: int = ROPE_HALF):
+    """Attention of rotated queries and keys: softmax(rope(Q) rope(K)^T scale) V.
+
+    cos, sin: [P, D/2] tables indexed by position; positions as ``rope_qk``.
+    Returns (O, LSE) as ``attention``.
+    """
+    qr, kr = rope_qk(q, k, cos, sin, causal, kv_lens, style)
     return attention(qr, kr, v, scale, causal, kv_lens)
 
 

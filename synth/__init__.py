@@ -99,3 +99,13 @@ def make_workload(w: Workload, seed: int = 0, device="cpu"):
 def make_do(B, H, Nq, D, dtype, seed: int = 0, device="cpu"):
     """Output gradient dO [B,H,Nq,D] ~ N(0, 1) for the backward pass."""
     return normal((B, H, Nq, D), dtype, seed, DO_ID, device)
+
+
+def rope_tables(n_pos: int, D: int, base: float = 10000.0, device="cpu"):
+    """RoPE cos/sin tables, fp32 [n_pos, D/2]: angle of position p and pair i
+    is p * base^(-2i/D), the usual frequency schedule (the tables are inputs
+    of the rotation; the method does not fix them)."""
+    inv = base ** (-torch.arange(0, D // 2, dtype=torch.float64) * 2.0 / D)
+    ang = torch.arange(n_pos, dtype=torch.float64)[:, None] * inv[None, :]
+    return (torch.cos(ang).to(torch.float32).to(device).contiguous(),
+            torch.sin(ang).to(torch.float32).to(device).contiguous())

@@ -34,7 +34,8 @@ def declared_functions():
 
 def test_header_declares_the_api():
     assert declared_functions() == sorted(
-        ["fa_forward", "fa_forward_masked", "fa_forward_f32", "fa_forward_f32_masked",
+        ["fa_forward", "fa_forward_masked", "fa_forward_f16", "fa_forward_f16_masked",
+         "fa_forward_f32", "fa_forward_f32_masked", "fa_rope", "fa_rope_workspace_bytes", "fa_forward_rope",
          "fa_decode_workspace_bytes", "fa_decode_splitkv", "fa_decode_splitkv_masked",
          "fa_backward_workspace_bytes", "fa_backward", "fa_backward_masked", "fa_status_string"])
 
@@ -59,7 +60,7 @@ def fwd(lib, fn="fa_forward", Q=FAKE, K=FAKE + 0x100000, V=FAKE + 0x200000, O=FA
     return getattr(lib, fn)(Q, K, V, O, L, B, H, Nq, Nk, D, scale, causal, None)
 
 
-@pytest.mark.parametrize("fn", ["fa_forward", "fa_forward_f32"])
+@pytest.mark.parametrize("fn", ["fa_forward", "fa_forward_f16", "fa_forward_f32"])
 def test_forward_rejects_bad_arguments(lib, fn):
     assert fwd(lib, fn, Q=None) == INVALID
     assert fwd(lib, fn, O=None) == INVALID
@@ -81,7 +82,7 @@ def test_forward_rejects_bad_arguments(lib, fn):
     assert fwd(lib, fn, causal=-1) == INVALID
 
 
-@pytest.mark.parametrize("fn", ["fa_forward_masked", "fa_forward_f32_masked"])
+@pytest.mark.parametrize("fn", ["fa_forward_masked", "fa_forward_f16_masked", "fa_forward_f32_masked"])
 def test_masked_forward_rejects_bad_kv_lens(lib, fn):
     def call(lens, **kw):
         a = dict(Q=FAKE, K=FAKE + 0x100000, V=FAKE + 0x200000, O=FAKE + 0x300000, L=None, B=2, H=1, Nq=16,
@@ -96,7 +97,7 @@ def test_masked_forward_rejects_bad_kv_lens(lib, fn):
     assert call(FAKE + 0x400000, B=0) == 0                            # nothing to do
 
 
-@pytest.mark.parametrize("fn", ["fa_forward", "fa_forward_f32"])
+@pytest.mark.parametrize("fn", ["fa_forward", "fa_forward_f16", "fa_forward_f32"])
 def test_forward_empty_problem_is_a_noop(lib, fn):
     # nothing to compute: returns before any pointer is looked at or any launch
     assert fwd(lib, fn, Q=None, K=None, V=None, O=None, B=0) == 0
@@ -190,6 +191,38 @@ def test_masked_backward_and_decode_reject_bad_kv_lens(lib):
     assert dm(FAKE + 0x500002) == INVALID                             # misaligned
     assert dm(FAKE + 0x400000 + 64) == INVALID                        # inside the workspace
     assert dm(FAKE + 0x300000) == INVALID                             # inside O
+
+
+def test_rope_rejects_bad_arguments(lib):
+    def rope(X=FAKE, Y=FAKE + 0x100000, C=FAKE + 0x200000, S=FAKE + 0x300000, n_pos=64, style=0, dtype=0, B=1,
+             H=2, N=64, D=128):
+        return lib.fa_rope(X, Y, C, S, n_pos, style, dtype, B, H, N, D, None)
+    assert rope(style=2) == INVALID
+    assert rope(dtype=3) == INVALID
+    assert rope(D=96) == UNSUPPORTED
+    assert rope(n_pos=63) == INVALID                                  # table shorter than N
+    assert rope(C=FAKE + 0x200004) == INVALID                         # misaligned table
+    assert rope(Y=FAKE + 0x40) == INVALID                             # partial overlap with X
+    assert rope(Y=FAKE + 0x200000) == INVALID                         # Y over the cos table
+    assert rope(X=None) == INVALID
+    assert rope(N=0, X=None, Y=None, C=None, S=None) == 0
+    assert lib.fa_rope_workspace_bytes(2, 3, 100, 64) == 2 * 3 * 100 * 64 * 2
+
+
+def test_forward_rope_rejects_bad_arguments(lib):
+    def fr(W=FAKE + 0x600000, wbytes=1 * 2 * 64 * 128 * 2, n_pos=64, C=FAKE + 0x400000, S=FAKE + 0x500000,
+           style=0, dtype=0, causal=0, Nq=64, Nk=64):
+        return lib.fa_forward_rope(FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, None, None, C, S,
+                                   n_pos, style, dtype, W, wbytes, 1, 2, Nq, Nk, 128, 0.1, causal, None)
+    assert fr(wbytes=100) == INVALID                                  # workspace too small
+    assert fr(W=None) == INVALID
+    assert fr(W=FAKE + 0x100000) == INVALID                           # workspace over K
+    assert fr(n_pos=63) == INVALID
+    assert fr(Nk=80, n_pos=70) == INVALID
+    assert fr(style=5) == INVALID
+    assert fr(dtype=2) == INVALID
+    assert fr(causal=7) == INVALID
+    assert fr(C=None) == INVALID
 
 
 def test_python_binding_refuses_cpu_tensors(lib):
