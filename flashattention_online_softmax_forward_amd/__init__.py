@@ -164,13 +164,16 @@ def fa_decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, num_spl
                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                       want_lse: bool = True, kv_lens: Optional[torch.Tensor] = None
                       ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Split-KV decode of one query token: q bf16 [B,H,1,D], k/v bf16 [B,H,Nk,D]
-    (of which the first kv_lens[b] keys are real, when given).
-    Returns (O bf16 [B,H,1,D], LSE fp32 [B,H] or None). ``workspace`` is a
-    device tensor of at least fa_decode_workspace_bytes(B,H,D,num_splits) bytes;
-    one is allocated when not given."""
+    """Split-KV decode of one query token: q [B,H,1,D], k/v [B,H,Nk,D], bf16 or
+    fp16 (of which the first kv_lens[b] keys are real, when given).
+    Returns (O [B,H,1,D] in the input type, LSE fp32 [B,H] or None).
+    ``workspace`` is a device tensor of at least
+    fa_decode_workspace_bytes(B,H,D,num_splits) bytes; one is allocated when
+    not given."""
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"q must be bfloat16 or float16 (got {q.dtype})")
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_tensor(name, t, torch.bfloat16)
+        _check_tensor(name, t, q.dtype)
     B, H, one, D = q.shape
     Nk = k.shape[2]
     if one != 1:
@@ -187,22 +190,25 @@ def fa_decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, num_spl
     ws_bytes = workspace.numel() * workspace.element_size()
     if out is None:
         out = torch.empty_like(q)
-    _check_tensor("out", out, torch.bfloat16)
+    _check_tensor("out", out, q.dtype)
     if lse is None and want_lse:
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
     if lse is not None:
         _check_tensor("lse", lse, torch.float32, ndim=2)
     kv_lens = _check_kv_lens(kv_lens, B, q.device)
     lse_p = lse.data_ptr() if lse is not None else None
+    lib = _lib.load()
+    name = "fa_decode_splitkv" + ("_f16" if q.dtype == torch.float16 else "")
     if kv_lens is None:
-        code = _lib.load().fa_decode_splitkv(
+        code = getattr(lib, name)(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_p, workspace.data_ptr(), ws_bytes,
             B, H, Nk, D, float(scale), int(num_splits), _stream(q))
     else:
-        code = _lib.load().fa_decode_splitkv_masked(
+        name += "_masked"
+        code = getattr(lib, name)(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_p, kv_lens.data_ptr(),
             workspace.data_ptr(), ws_bytes, B, H, Nk, D, float(scale), int(num_splits), _stream(q))
-    _lib.check(code, "fa_decode_splitkv")
+    _lib.check(code, name)
     return out, lse
 
 
@@ -216,13 +222,15 @@ def fa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tens
                 dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
                 dv: Optional[torch.Tensor] = None, kv_lens: Optional[torch.Tensor] = None
                 ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """bf16 backward with recompute: q, o, do [B,H,Nq,D], k, v [B,H,Nk,D], lse
-    fp32 [B,H,Nq] (the forward's, same scale and causal flag). Returns
-    (dQ, dK, dV) in bf16 with the shapes of q, k, v. ``workspace`` holds at
-    least fa_backward_workspace_bytes(B,H,Nq) bytes; one is allocated when not
-    given."""
+    """Backward with recompute, bf16 or fp16: q, o, do [B,H,Nq,D], k, v
+    [B,H,Nk,D], lse fp32 [B,H,Nq] (the forward's, same scale, causal and
+    kv_lens). Returns (dQ, dK, dV) in the input type with the shapes of q, k,
+    v. ``workspace`` holds at least fa_backward_workspace_bytes(B,H,Nq) bytes;
+    one is allocated when not given."""
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"q must be bfloat16 or float16 (got {q.dtype})")
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
-        _check_tensor(name, t, torch.bfloat16)
+        _check_tensor(name, t, q.dtype)
     B, H, Nq, D = q.shape
     Nk = k.shape[2]
     if tuple(k.shape) != (B, H, Nk, D) or tuple(v.shape) != (B, H, Nk, D):
@@ -244,19 +252,22 @@ def fa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tens
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
-        _check_tensor(name, t, torch.bfloat16)
+        _check_tensor(name, t, q.dtype)
         if tuple(t.shape) != tuple(ref.shape):
             raise ValueError(f"{name} must have the shape {tuple(ref.shape)}")
     mode = _causal_mode(causal)
     kv_lens = _check_kv_lens(kv_lens, B, q.device)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr())
     outs = (dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), ws_bytes)
+    lib = _lib.load()
+    name = "fa_backward" + ("_f16" if q.dtype == torch.float16 else "")
     if kv_lens is None:
-        code = _lib.load().fa_backward(*ptrs, *outs, B, H, Nq, Nk, D, float(scale), mode, _stream(q))
+        code = getattr(lib, name)(*ptrs, *outs, B, H, Nq, Nk, D, float(scale), mode, _stream(q))
     else:
-        code = _lib.load().fa_backward_masked(*ptrs, kv_lens.data_ptr(), *outs, B, H, Nq, Nk, D, float(scale),
-                                              mode, _stream(q))
-    _lib.check(code, "fa_backward")
+        name += "_masked"
+        code = getattr(lib, name)(*ptrs, kv_lens.data_ptr(), *outs, B, H, Nq, Nk, D, float(scale), mode,
+                                  _stream(q))
+    _lib.check(code, name)
     return dq, dk, dv
 
 

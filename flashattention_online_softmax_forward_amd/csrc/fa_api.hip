@@ -201,9 +201,13 @@ size_t fa_decode_workspace_bytes(int B, int H, int D, int num_splits) {
     return (size_t)B * H * num_splits * (D + 2) * sizeof(float);
 }
 
-fa_status fa_decode_splitkv_masked(const void* Q, const void* K, const void* V, void* O, float* LSE,
-                                   const int* kv_lens, void* workspace, size_t workspace_bytes, int B, int H,
-                                   int Nk, int D, float scale, int num_splits, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+fa_status decode_impl(const void* Q, const void* K, const void* V, void* O, float* LSE, const int* kv_lens,
+                      void* workspace, size_t workspace_bytes, int B, int H, int Nk, int D, float scale,
+                      int num_splits, hipStream_t stream, bool f16) {
     if (B < 0 || H < 0 || Nk < 0 || num_splits < 1) return FA_ERR_INVALID_ARG;
     if (!good_scale(scale)) return FA_ERR_INVALID_ARG;
     if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
@@ -229,8 +233,34 @@ fa_status fa_decode_splitkv_masked(const void* Q, const void* K, const void* V, 
         return FA_ERR_INVALID_ARG;
     float* ws_o = static_cast<float*>(workspace);
     float* ws_ml = ws_o + (size_t)B * H * num_splits * D;
-    const fa::DecodeArgs a{Q, K, V, O, LSE, ws_o, ws_ml, kv_lens, B, H, Nk, D, num_splits, scale, stream};
+    fa::DecodeArgs a{Q, K, V, O, LSE, ws_o, ws_ml, kv_lens, B, H, Nk, D, num_splits, scale, stream};
+    a.f16 = f16;
     return fa::launch_decode(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_decode_splitkv_masked(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                                   const int* kv_lens, void* workspace, size_t workspace_bytes, int B, int H,
+                                   int Nk, int D, float scale, int num_splits, hipStream_t stream) {
+    return decode_impl(Q, K, V, O, LSE, kv_lens, workspace, workspace_bytes, B, H, Nk, D, scale, num_splits,
+                       stream, false);
+}
+
+fa_status fa_decode_splitkv_f16_masked(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                                       const int* kv_lens, void* workspace, size_t workspace_bytes, int B, int H,
+                                       int Nk, int D, float scale, int num_splits, hipStream_t stream) {
+    return decode_impl(Q, K, V, O, LSE, kv_lens, workspace, workspace_bytes, B, H, Nk, D, scale, num_splits,
+                       stream, true);
+}
+
+fa_status fa_decode_splitkv_f16(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                                void* workspace, size_t workspace_bytes, int B, int H, int Nk, int D,
+                                float scale, int num_splits, hipStream_t stream) {
+    return decode_impl(Q, K, V, O, LSE, nullptr, workspace, workspace_bytes, B, H, Nk, D, scale, num_splits,
+                       stream, true);
 }
 
 fa_status fa_decode_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE,
@@ -245,10 +275,14 @@ size_t fa_backward_workspace_bytes(int B, int H, int Nq) {
     return (size_t)B * H * Nq * sizeof(float);
 }
 
-fa_status fa_backward_masked(const void* Q, const void* K, const void* V, const void* O, const void* dO,
-                             const float* LSE, const int* kv_lens, void* dQ, void* dK, void* dV, void* workspace,
-                             size_t workspace_bytes, int B, int H, int Nq, int Nk, int D, float scale,
-                             int causal, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+fa_status backward_impl(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                        const float* LSE, const int* kv_lens, void* dQ, void* dK, void* dV, void* workspace,
+                        size_t workspace_bytes, int B, int H, int Nq, int Nk, int D, float scale, int causal,
+                        hipStream_t stream, bool f16) {
     if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return FA_ERR_INVALID_ARG;
     if (!good_scale(scale) || !good_causal(causal)) return FA_ERR_INVALID_ARG;
     if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
@@ -289,9 +323,38 @@ fa_status fa_backward_masked(const void* Q, const void* K, const void* V, const 
             overlaps(kv_lens, (size_t)B * 4, workspace, need))
             return FA_ERR_INVALID_ARG;
     }
-    const fa::BwdArgs a{Q, K, V, O, dO, LSE, dQ, dK, dV, static_cast<float*>(workspace), kv_lens,
-                        B, H, Nq, Nk, D, scale, causal, stream};
+    fa::BwdArgs a{Q, K, V, O, dO, LSE, dQ, dK, dV, static_cast<float*>(workspace), kv_lens,
+                  B, H, Nq, Nk, D, scale, causal, stream};
+    a.f16 = f16;
     return fa::launch_bwd(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_backward_masked(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                             const float* LSE, const int* kv_lens, void* dQ, void* dK, void* dV, void* workspace,
+                             size_t workspace_bytes, int B, int H, int Nq, int Nk, int D, float scale,
+                             int causal, hipStream_t stream) {
+    return backward_impl(Q, K, V, O, dO, LSE, kv_lens, dQ, dK, dV, workspace, workspace_bytes, B, H, Nq, Nk, D,
+                         scale, causal, stream, false);
+}
+
+fa_status fa_backward_f16_masked(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                                 const float* LSE, const int* kv_lens, void* dQ, void* dK, void* dV,
+                                 void* workspace, size_t workspace_bytes, int B, int H, int Nq, int Nk, int D,
+                                 float scale, int causal, hipStream_t stream) {
+    return backward_impl(Q, K, V, O, dO, LSE, kv_lens, dQ, dK, dV, workspace, workspace_bytes, B, H, Nq, Nk, D,
+                         scale, causal, stream, true);
+}
+
+fa_status fa_backward_f16(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                          const float* LSE, void* dQ, void* dK, void* dV, void* workspace,
+                          size_t workspace_bytes, int B, int H, int Nq, int Nk, int D, float scale,
+                          int causal, hipStream_t stream) {
+    return backward_impl(Q, K, V, O, dO, LSE, nullptr, dQ, dK, dV, workspace, workspace_bytes, B, H, Nq, Nk, D,
+                         scale, causal, stream, true);
 }
 
 fa_status fa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,

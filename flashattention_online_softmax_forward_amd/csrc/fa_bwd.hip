@@ -9,7 +9,8 @@
 // Exponentials are base 2 (scale and L multiplied by log2 e).
 //
 // gfx950 mapping (own design, on the forward kernel's MFMA layouts):
-//   * Both product kernels use v_mfma_f32_32x32x16_bf16 with 4 waves x 32
+//   * bf16 or fp16 inputs (Elem<T>: MFMA, transpose read, packing).
+//   * Both product kernels use v_mfma_f32_32x32x16_bf16 (_f16) with 4 waves x 32
 //     rows per workgroup and stream the other operand through LDS in tiles of
 //     32 rows (global_load_lds_dwordx4 DMA, double-buffered, one barrier per
 //     tile).
@@ -134,38 +135,42 @@ struct TileOffsets {
     }
 };
 
-template <int D>
-__device__ __forceinline__ bf16x8_t row_operand(const uint16_t* tile, const TileOffsets<D>& o, int kk) {
-    return *(LDS_AS const bf16x8_t*)((LDS_AS const char*)(LDS_AS const uint16_t*)tile + o.row[kk]);
+template <typename T, int D>
+__device__ __forceinline__ typename Elem<T>::v8 row_operand(const uint16_t* tile, const TileOffsets<D>& o, int kk) {
+    using V8 = typename Elem<T>::v8;
+    return *(LDS_AS const V8*)((LDS_AS const char*)(LDS_AS const uint16_t*)tile + o.row[kk]);
 }
 
-template <int D>
-__device__ __forceinline__ bf16x8_t tr_operand(const uint16_t* tile, const TileOffsets<D>& o, int tt, int db) {
-    bf16x4_t part[2];
+template <typename T, int D>
+__device__ __forceinline__ typename Elem<T>::v8 tr_operand(const uint16_t* tile, const TileOffsets<D>& o, int tt, int db) {
+    using V4 = typename Elem<T>::v4;
+    using V8 = typename Elem<T>::v8;
+    V4 part[2];
 #pragma unroll
     for (int rd = 0; rd < 2; ++rd)
-        part[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (LDS_AS bf16x4_t*)((LDS_AS char*)(LDS_AS uint16_t*)tile + o.tr[db * 2 + rd] + (uint32_t)(tt * 16 * D * 2)));
-    return bf16x8_t{part[0][0], part[0][1], part[0][2], part[0][3],
+        part[rd] = Elem<T>::tr_read(
+            (LDS_AS V4*)((LDS_AS char*)(LDS_AS uint16_t*)tile + o.tr[db * 2 + rd] + (uint32_t)(tt * 16 * D * 2)));
+    return V8{part[0][0], part[0][1], part[0][2], part[0][3],
                     part[1][0], part[1][1], part[1][2], part[1][3]};
 }
 
 // Row `row` of a [*, D] array as MFMA B operands: lane (j, h) holds elements
 // 16*kk + 8*h .. +7 (zero when the row is past the end).
-template <int D>
-__device__ __forceinline__ void load_b_rows(const uint16_t* base, int row, bool valid, int h, bf16x8_t* out) {
+template <typename T, int D>
+__device__ __forceinline__ void load_b_rows(const uint16_t* base, int row, bool valid, int h,
+                                            typename Elem<T>::v8* out) {
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
         u32x4_t w = {0u, 0u, 0u, 0u};
         if (valid) w = *(const u32x4_t*)(base + (size_t)row * D + kk * 16 + h * 8);
-        out[kk] = __builtin_bit_cast(bf16x8_t, w);
+        out[kk] = __builtin_bit_cast(typename Elem<T>::v8, w);
     }
 }
 
 // Store an fp32 accumulator of 32 rows x D held transposed (lane j = row,
 // register r of block db = column 32*db + 8*(r/4) + 4*h + r%4) as bf16,
 // multiplied by `mul`.
-template <int D>
+template <typename T, int D>
 __device__ __forceinline__ void store_rows(uint16_t* rowp, const f32x16_t* acc, int h, float mul) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -173,8 +178,8 @@ __device__ __forceinline__ void store_rows(uint16_t* rowp, const f32x16_t* acc, 
         for (int a4 = 0; a4 < 4; ++a4) {
             const int d = db * 32 + a4 * 8 + h * 4;
             u32x2_t w;
-            w[0] = pack_bf16x2(acc[db][a4 * 4 + 0] * mul, acc[db][a4 * 4 + 1] * mul);
-            w[1] = pack_bf16x2(acc[db][a4 * 4 + 2] * mul, acc[db][a4 * 4 + 3] * mul);
+            w[0] = Elem<T>::pack2(acc[db][a4 * 4 + 0] * mul, acc[db][a4 * 4 + 1] * mul);
+            w[1] = Elem<T>::pack2(acc[db][a4 * 4 + 2] * mul, acc[db][a4 * 4 + 3] * mul);
             *(u32x2_t*)(rowp + d) = w;
         }
 }
@@ -184,12 +189,12 @@ __device__ __forceinline__ void store_rows(uint16_t* rowp, const f32x16_t* acc, 
 // registers a phase holds.
 template <int N, int LEAD, typename Op, typename Step>
 __device__ __forceinline__ void mfma_stream(Op op, Step step) {
-    bf16x8_t ring[LEAD];
+    decltype(op(0)) ring[LEAD];
 #pragma unroll
     for (int i = 0; i < LEAD && i < N; ++i) ring[i] = op(i);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-        const bf16x8_t a = ring[i % LEAD];
+        const auto a = ring[i % LEAD];
         if (i + LEAD < N) ring[i % LEAD] = op(i + LEAD);
         step(i, a);
         __builtin_amdgcn_sched_barrier(0);
@@ -199,7 +204,7 @@ __device__ __forceinline__ void mfma_stream(Op op, Step step) {
 }  // namespace
 
 // D_i = sum_d dO[i,d] O[i,d] in fp32: D/8 lanes per row, 8 elements each.
-template <int D>
+template <typename T, int D>
 __global__ __launch_bounds__(256)
 void bwd_rowdot_kernel(const uint16_t* __restrict__ Og, const uint16_t* __restrict__ dOg,
                        float* __restrict__ Dg, long long rows) {
@@ -213,8 +218,8 @@ void bwd_rowdot_kernel(const uint16_t* __restrict__ Og, const uint16_t* __restri
         const u32x4_t b = *(const u32x4_t*)(dOg + row * D + sub * 8);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            acc = __builtin_fmaf(bf16_lo(a[i]), bf16_lo(b[i]), acc);
-            acc = __builtin_fmaf(bf16_hi(a[i]), bf16_hi(b[i]), acc);
+            acc = __builtin_fmaf(Elem<T>::lo(a[i]), Elem<T>::lo(b[i]), acc);
+            acc = __builtin_fmaf(Elem<T>::hi(a[i]), Elem<T>::hi(b[i]), acc);
         }
     }
     acc = group_sum<LPR>(acc);
@@ -222,13 +227,14 @@ void bwd_rowdot_kernel(const uint16_t* __restrict__ Og, const uint16_t* __restri
 }
 
 // dQ for 128 query rows of one (batch, head), streaming K and V tiles.
-template <int D>
+template <typename T, int D>
 __global__ __launch_bounds__(kBwdThreads, 2)
 void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                    const uint16_t* __restrict__ Vg, const uint16_t* __restrict__ dOg,
                    const float* __restrict__ LSEg, const float* __restrict__ Dg,
                    uint16_t* __restrict__ dQg, const int* __restrict__ kv_lens, int H, int Nq, int Nk,
                    int nqb, float scale, float scale2, int causal) {
+    using V8 = typename Elem<T>::v8;
     constexpr int NKK = D / 16, NDB = D / 32;
     constexpr int TILE = kBT * D;
     const bool CAUSAL = causal != kCausalNone;
@@ -258,9 +264,9 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
     const int Lk = real_keys(kv_lens, bh / H, Nk);
     const int doff = causal == kCausalBottomRight ? Lk - Nq : 0;   // key j visible from query i iff j <= i + doff
 
-    bf16x8_t qf[NKK], dof[NKK];
-    load_b_rows<D>(Qg + (size_t)bh * Nq * D, qrow, qvalid, h, qf);
-    load_b_rows<D>(dOg + (size_t)bh * Nq * D, qrow, qvalid, h, dof);
+    V8 qf[NKK], dof[NKK];
+    load_b_rows<T, D>(Qg + (size_t)bh * Nq * D, qrow, qvalid, h, qf);
+    load_b_rows<T, D>(dOg + (size_t)bh * Nq * D, qrow, qvalid, h, dof);
     const float l2 = qvalid ? LSEg[(size_t)bh * Nq + qrow] * kLog2e : 0.f;
     const float dr = qvalid ? Dg[(size_t)bh * Nq + qrow] : 0.f;
 
@@ -289,12 +295,12 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
         f32x16_t s = {}, dp = {};
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(kt, off, kk), qf[kk], s, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(vt, off, kk), dof[kk], dp, 0, 0, 0);
+            s = Elem<T>::mfma(row_operand<T, D>(kt, off, kk), qf[kk], s);
+            dp = Elem<T>::mfma(row_operand<T, D>(vt, off, kk), dof[kk], dp);
         }
         const int kv0 = t * kBT;
         const bool edge = kv0 + kBT > Lk || (CAUSAL && kv0 + kBT - 1 > wrow0 + doff);
-        bf16x8_t dsf[2];
+        V8 dsf[2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             float ds[8];
@@ -309,18 +315,18 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
                 ds[e] = p * (dp[r] - dr);
             }
             u32x4_t w;
-            w[0] = pack_bf16x2(ds[0], ds[1]);
-            w[1] = pack_bf16x2(ds[2], ds[3]);
-            w[2] = pack_bf16x2(ds[4], ds[5]);
-            w[3] = pack_bf16x2(ds[6], ds[7]);
-            dsf[tt] = __builtin_bit_cast(bf16x8_t, w);
+            w[0] = Elem<T>::pack2(ds[0], ds[1]);
+            w[1] = Elem<T>::pack2(ds[2], ds[3]);
+            w[2] = Elem<T>::pack2(ds[4], ds[5]);
+            w[3] = Elem<T>::pack2(ds[6], ds[7]);
+            dsf[tt] = __builtin_bit_cast(V8, w);
         }
         // dQ^T += K^T dS^T.
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(kt, off, tt, db), dsf[tt], acc[db], 0, 0, 0);
+                acc[db] = Elem<T>::mfma(tr_operand<T, D>(kt, off, tt, db), dsf[tt], acc[db]);
     };
 
     if (ntiles > 0) stage(0, k_lds0, v_lds0);
@@ -340,17 +346,18 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
         __syncthreads();
     }
 
-    if (qvalid) store_rows<D>(dQg + ((size_t)bh * Nq + qrow) * D, acc, h, scale);
+    if (qvalid) store_rows<T, D>(dQg + ((size_t)bh * Nq + qrow) * D, acc, h, scale);
 }
 
 // dK and dV for 128 keys of one (batch, head), streaming Q, dO, L and D tiles.
-template <int D>
+template <typename T, int D>
 __global__ __launch_bounds__(kBwdThreads, 2)
 void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                      const uint16_t* __restrict__ Vg, const uint16_t* __restrict__ dOg,
                      const float* __restrict__ LSEg, const float* __restrict__ Dg,
                      uint16_t* __restrict__ dKg, uint16_t* __restrict__ dVg, const int* __restrict__ kv_lens,
                      int H, int Nq, int Nk, int nkb, float scale, float scale2, int causal) {
+    using V8 = typename Elem<T>::v8;
     constexpr int NKK = D / 16, NDB = D / 32, CPR = D / 8;
     constexpr int TILE = kBT * D;
     const bool CAUSAL = causal != kCausalNone;
@@ -385,8 +392,8 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     const float* L = LSEg + (size_t)bh * Nq;
     const float* Dv = Dg + (size_t)bh * Nq;
 
-    bf16x8_t kf[NKK];
-    load_b_rows<D>(Kg + (size_t)bh * Nk * D, krow, kvalid, h, kf);
+    V8 kf[NKK];
+    load_b_rows<T, D>(Kg + (size_t)bh * Nk * D, krow, kvalid, h, kf);
     TileOffsets<D> off;
     off.init(lane);
     // V rows of this wave as MFMA B operands of dP = dO V^T: lane (j, h)
@@ -436,20 +443,20 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
         stage_rows<D>(dO + (size_t)q0 * D, kBT, Nq - 1 - q0, od, wave, lane);
     };
     auto v_operand = [&](int kk) __attribute__((always_inline)) {
-        return *(LDS_AS const bf16x8_t*)((LDS_AS const char*)(LDS_AS const uint16_t*)v_blk + voff[kk]);
+        return *(LDS_AS const V8*)((LDS_AS const char*)(LDS_AS const uint16_t*)v_blk + voff[kk]);
     };
     // One tile in phases with their own live registers (sched_barrier between
     // them): S = Q K^T, P, dV^T += dO^T P, dP = dO V^T, dS, dK^T += Q^T dS.
     auto compute = [&](int u, const uint16_t* qt, const uint16_t* ot, int buf) __attribute__((always_inline)) {
         constexpr int LEAD = 2;
         f32x16_t s = {};
-        mfma_stream<NKK, LEAD>([&](int kk) { return row_operand<D>(qt, off, kk); },
-                               [&](int kk, bf16x8_t a) { s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[kk], s, 0, 0, 0); });
+        mfma_stream<NKK, LEAD>([&](int kk) { return row_operand<T, D>(qt, off, kk); },
+                               [&](int kk, V8 a) { s = Elem<T>::mfma(a, kf[kk], s); });
         const int q0 = u * kBT;
         const bool edge = q0 + kBT > Nq || kw0 + 32 > Lk || (CAUSAL && q0 + doff < kw0 + 31);
         // P (fp32, kept for dS) and its bf16 copy. Register r of lane (j, h)
         // is query 16*(r/8) + 8*h + r%8 of the tile.
-        bf16x8_t pf[2];
+        V8 pf[2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             const f32x4_t la = *(const f32x4_t*)&ld_lds[buf][tt * 16 + h * 8];
@@ -465,23 +472,23 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
                 s[r] = p;
             }
             u32x4_t w;
-            w[0] = pack_bf16x2(s[tt * 8 + 0], s[tt * 8 + 1]);
-            w[1] = pack_bf16x2(s[tt * 8 + 2], s[tt * 8 + 3]);
-            w[2] = pack_bf16x2(s[tt * 8 + 4], s[tt * 8 + 5]);
-            w[3] = pack_bf16x2(s[tt * 8 + 6], s[tt * 8 + 7]);
-            pf[tt] = __builtin_bit_cast(bf16x8_t, w);
+            w[0] = Elem<T>::pack2(s[tt * 8 + 0], s[tt * 8 + 1]);
+            w[1] = Elem<T>::pack2(s[tt * 8 + 2], s[tt * 8 + 3]);
+            w[2] = Elem<T>::pack2(s[tt * 8 + 4], s[tt * 8 + 5]);
+            w[3] = Elem<T>::pack2(s[tt * 8 + 6], s[tt * 8 + 7]);
+            pf[tt] = __builtin_bit_cast(V8, w);
         }
         __builtin_amdgcn_sched_barrier(0);
-        mfma_stream<2 * NDB, LEAD>([&](int i) { return tr_operand<D>(ot, off, i / NDB, i % NDB); },
-                                   [&](int i, bf16x8_t a) {
-                                       adv[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[i / NDB], adv[i % NDB], 0, 0, 0);
+        mfma_stream<2 * NDB, LEAD>([&](int i) { return tr_operand<T, D>(ot, off, i / NDB, i % NDB); },
+                                   [&](int i, V8 a) {
+                                       adv[i % NDB] = Elem<T>::mfma(a, pf[i / NDB], adv[i % NDB]);
                                    });
         f32x16_t dp = {};
-        mfma_stream<NKK, LEAD>([&](int kk) { return row_operand<D>(ot, off, kk); },
-                               [&](int kk, bf16x8_t a) {
-                                   dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, v_operand(kk), dp, 0, 0, 0);
+        mfma_stream<NKK, LEAD>([&](int kk) { return row_operand<T, D>(ot, off, kk); },
+                               [&](int kk, V8 a) {
+                                   dp = Elem<T>::mfma(a, v_operand(kk), dp);
                                });
-        bf16x8_t dsf[2];
+        V8 dsf[2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             const f32x4_t da = *(const f32x4_t*)&ld_lds[buf][kBT + tt * 16 + h * 8];
@@ -493,16 +500,16 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
                 ds[e] = s[r] * (dp[r] - (e < 4 ? da[e] : dbv[e - 4]));
             }
             u32x4_t x;
-            x[0] = pack_bf16x2(ds[0], ds[1]);
-            x[1] = pack_bf16x2(ds[2], ds[3]);
-            x[2] = pack_bf16x2(ds[4], ds[5]);
-            x[3] = pack_bf16x2(ds[6], ds[7]);
-            dsf[tt] = __builtin_bit_cast(bf16x8_t, x);
+            x[0] = Elem<T>::pack2(ds[0], ds[1]);
+            x[1] = Elem<T>::pack2(ds[2], ds[3]);
+            x[2] = Elem<T>::pack2(ds[4], ds[5]);
+            x[3] = Elem<T>::pack2(ds[6], ds[7]);
+            dsf[tt] = __builtin_bit_cast(V8, x);
         }
         __builtin_amdgcn_sched_barrier(0);
-        mfma_stream<2 * NDB, LEAD>([&](int i) { return tr_operand<D>(qt, off, i / NDB, i % NDB); },
-                                   [&](int i, bf16x8_t a) {
-                                       adk[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsf[i / NDB], adk[i % NDB], 0, 0, 0);
+        mfma_stream<2 * NDB, LEAD>([&](int i) { return tr_operand<T, D>(qt, off, i / NDB, i % NDB); },
+                                   [&](int i, V8 a) {
+                                       adk[i % NDB] = Elem<T>::mfma(a, dsf[i / NDB], adk[i % NDB]);
                                    });
     };
 
@@ -537,23 +544,23 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     }
 
     if (kvalid) {
-        store_rows<D>(dKg + ((size_t)bh * Nk + krow) * D, adk, h, scale);
-        store_rows<D>(dVg + ((size_t)bh * Nk + krow) * D, adv, h, 1.0f);
+        store_rows<T, D>(dKg + ((size_t)bh * Nk + krow) * D, adk, h, scale);
+        store_rows<T, D>(dVg + ((size_t)bh * Nk + krow) * D, adv, h, 1.0f);
     }
 }
 
-template <int D>
+template <typename T, int D>
 static hipError_t launch_bwd_d(const BwdArgs& a) {
     const float scale2 = a.scale * kLog2e;
     if (a.Nq > 0) {
         const long long rows = (long long)a.B * a.H * a.Nq;
         constexpr int RPB = 256 / (D / 8);
-        hipLaunchKernelGGL((bwd_rowdot_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
+        hipLaunchKernelGGL((bwd_rowdot_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
                            a.stream, (const uint16_t*)a.O, (const uint16_t*)a.dO, a.Dvec, rows);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const int nqb = (a.Nq + BM_BWD - 1) / BM_BWD;
-        hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3(a.B * a.H * nqb), dim3(kBwdThreads), 0, a.stream,
+        hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3(a.B * a.H * nqb), dim3(kBwdThreads), 0, a.stream,
                            (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
                            (const uint16_t*)a.dO, a.LSE, a.Dvec, (uint16_t*)a.dQ, a.kv_lens, a.H, a.Nq, a.Nk,
                            nqb, a.scale, scale2, a.causal);
@@ -563,7 +570,7 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
     // With Nq = 0 the dK/dV kernel stages only V, runs no query tile and
     // stores zeros.
     const int nkb = (a.Nk + BM_BWD - 1) / BM_BWD;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(a.B * a.H * nkb), dim3(kBwdThreads), 0, a.stream,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D>), dim3(a.B * a.H * nkb), dim3(kBwdThreads), 0, a.stream,
                        (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
                        (const uint16_t*)a.dO, a.LSE, a.Dvec, (uint16_t*)a.dK, (uint16_t*)a.dV, a.kv_lens,
                        a.H, a.Nq, a.Nk, nkb, a.scale, scale2, a.causal);
@@ -571,7 +578,8 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
 }
 
 hipError_t launch_bwd(const BwdArgs& a) {
-    return a.D == 128 ? launch_bwd_d<128>(a) : launch_bwd_d<64>(a);
+    if (a.f16) return a.D == 128 ? launch_bwd_d<_Float16, 128>(a) : launch_bwd_d<_Float16, 64>(a);
+    return a.D == 128 ? launch_bwd_d<__bf16, 128>(a) : launch_bwd_d<__bf16, 64>(a);
 }
 
 }  // namespace fa

@@ -1,5 +1,6 @@
 // Split-KV decode for gfx950: one query token per (batch, head) over a long
-// key/value cache (the "Flash-decoding" exercise of the ML compiler page).
+// key/value cache (the "Flash-decoding" exercise of the ML compiler page),
+// bf16 or fp16 (Elem<T> widens the inputs and rounds O).
 //
 // Kernel 1 (partial): one workgroup per (head, key chunk). The chunk's keys are
 // streamed once from HBM with fully coalesced 16-byte loads: D/8 lanes share a
@@ -29,7 +30,7 @@ namespace fa {
 constexpr int kDecThreads = 256;
 constexpr int kDecUnroll = 4;
 
-template <int D>
+template <typename T, int D>
 __global__ __launch_bounds__(kDecThreads)
 void decode_partial_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                            const uint16_t* __restrict__ Vg, float* __restrict__ ws_o,
@@ -63,8 +64,8 @@ void decode_partial_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __re
         const u32x4_t w = *(const u32x4_t*)(Qg + (size_t)bh * D + sub * 8);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            q[2 * i] = bf16_lo(w[i]) * scale2;
-            q[2 * i + 1] = bf16_hi(w[i]) * scale2;
+            q[2 * i] = Elem<T>::lo(w[i]) * scale2;
+            q[2 * i + 1] = Elem<T>::hi(w[i]) * scale2;
         }
     }
 
@@ -92,8 +93,8 @@ void decode_partial_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __re
             float acc = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                acc = __builtin_fmaf(q[2 * i], bf16_lo(kr[u][i]), acc);
-                acc = __builtin_fmaf(q[2 * i + 1], bf16_hi(kr[u][i]), acc);
+                acc = __builtin_fmaf(q[2 * i], Elem<T>::lo(kr[u][i]), acc);
+                acc = __builtin_fmaf(q[2 * i + 1], Elem<T>::hi(kr[u][i]), acc);
             }
             acc = group_sum<LPK>(acc);
             sc[u] = (base + u * G < j1) ? acc : -INFINITY;
@@ -117,8 +118,8 @@ void decode_partial_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __re
             float lo = o[2 * i] * alpha, hi = o[2 * i + 1] * alpha;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                lo = __builtin_fmaf(p[u], bf16_lo(vr[u][i]), lo);
-                hi = __builtin_fmaf(p[u], bf16_hi(vr[u][i]), hi);
+                lo = __builtin_fmaf(p[u], Elem<T>::lo(vr[u][i]), lo);
+                hi = __builtin_fmaf(p[u], Elem<T>::hi(vr[u][i]), hi);
             }
             o[2 * i] = lo;
             o[2 * i + 1] = hi;
@@ -160,7 +161,7 @@ constexpr int kCombThreads = 256;
 // Combine: 256 threads per (batch, head); thread = (split group sg, column
 // quad dq). Each thread folds splits sg, sg + SG, ... of its 4 columns (float4
 // loads, several in flight), then the SG partial states are merged in LDS.
-template <int D>
+template <typename T, int D>
 __global__ __launch_bounds__(kCombThreads)
 void decode_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
                            uint16_t* __restrict__ Og, float* __restrict__ LSEg, int S) {
@@ -215,26 +216,27 @@ void decode_combine_kernel(const float* __restrict__ ws_o, const float* __restri
             ot += sm_o[g * D + tid];
         }
         // No real key at all (every chunk empty): O = 0, LSE = -inf.
-        Og[(size_t)bh * D + tid] = __builtin_bit_cast(uint16_t, (__bf16)(lt > 0.f ? ot / lt : 0.f));
+        Og[(size_t)bh * D + tid] = (uint16_t)Elem<T>::pack2(lt > 0.f ? ot / lt : 0.f, 0.f);
         if (tid == 0 && LSEg) LSEg[bh] = lt > 0.f ? (M + __log2f(lt)) * kLn2 : -INFINITY;
     }
 }
 
-template <int D>
+template <typename T, int D>
 static hipError_t launch_d(const DecodeArgs& a) {
     const int BH = a.B * a.H;
-    hipLaunchKernelGGL((decode_partial_kernel<D>), dim3(BH * a.S), dim3(kDecThreads), 0, a.stream,
+    hipLaunchKernelGGL((decode_partial_kernel<T, D>), dim3(BH * a.S), dim3(kDecThreads), 0, a.stream,
                        (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V, a.ws_o, a.ws_ml,
                        a.kv_lens, a.H, a.Nk, a.S, a.scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(BH), dim3(kCombThreads), 0, a.stream, a.ws_o,
+    hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(BH), dim3(kCombThreads), 0, a.stream, a.ws_o,
                        a.ws_ml, (uint16_t*)a.O, a.LSE, a.S);
     return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs& a) {
-    return a.D == 128 ? launch_d<128>(a) : launch_d<64>(a);
+    if (a.f16) return a.D == 128 ? launch_d<_Float16, 128>(a) : launch_d<_Float16, 64>(a);
+    return a.D == 128 ? launch_d<__bf16, 128>(a) : launch_d<__bf16, 64>(a);
 }
 
 }  // namespace fa

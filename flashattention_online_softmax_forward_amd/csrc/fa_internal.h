@@ -66,6 +66,7 @@ struct DecodeArgs {
     int B, H, Nk, D, S;
     float scale;
     hipStream_t stream;
+    bool f16 = false;     // element type: fp16 (else bf16)
 };
 
 struct BwdArgs {
@@ -84,6 +85,7 @@ struct BwdArgs {
     float scale;
     int causal;           // kCausalNone / kCausalTopLeft / kCausalBottomRight
     hipStream_t stream;
+    bool f16 = false;     // element type: fp16 (else bf16)
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a);

@@ -223,6 +223,18 @@ fa_status fa_decode_splitkv_masked(const void* Q, const void* K, const void* V,
                                    int B, int H, int Nk, int D,
                                    float scale, int num_splits, hipStream_t stream);
 
+/* fa_decode_splitkv and fa_decode_splitkv_masked for fp16 Q, K, V and O. */
+fa_status fa_decode_splitkv_f16(const void* Q, const void* K, const void* V,
+                                void* O, float* LSE,
+                                void* workspace, size_t workspace_bytes,
+                                int B, int H, int Nk, int D,
+                                float scale, int num_splits, hipStream_t stream);
+fa_status fa_decode_splitkv_f16_masked(const void* Q, const void* K, const void* V,
+                                       void* O, float* LSE, const int* kv_lens,
+                                       void* workspace, size_t workspace_bytes,
+                                       int B, int H, int Nk, int D,
+                                       float scale, int num_splits, hipStream_t stream);
+
 /*
  * Bytes of device workspace fa_backward needs: B*H*Nq*4 (one fp32 value per
  * query row, D_i = sum_d dO[i,d] * O[i,d]). Returns 0 for invalid arguments.
@@ -274,6 +286,23 @@ fa_status fa_backward_masked(const void* Q, const void* K, const void* V,
                              void* workspace, size_t workspace_bytes,
                              int B, int H, int Nq, int Nk, int D,
                              float scale, int causal, hipStream_t stream);
+
+/* fa_backward and fa_backward_masked for fp16 inputs and gradients (the O and
+ * LSE of fa_forward_f16 / fa_forward_f16_masked); fp16 MFMA, P and dS rounded
+ * to fp16. */
+fa_status fa_backward_f16(const void* Q, const void* K, const void* V,
+                          const void* O, const void* dO, const float* LSE,
+                          void* dQ, void* dK, void* dV,
+                          void* workspace, size_t workspace_bytes,
+                          int B, int H, int Nq, int Nk, int D,
+                          float scale, int causal, hipStream_t stream);
+fa_status fa_backward_f16_masked(const void* Q, const void* K, const void* V,
+                                 const void* O, const void* dO, const float* LSE,
+                                 const int* kv_lens,
+                                 void* dQ, void* dK, void* dV,
+                                 void* workspace, size_t workspace_bytes,
+                                 int B, int H, int Nq, int Nk, int D,
+                                 float scale, int causal, hipStream_t stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa_status_string(fa_status s);

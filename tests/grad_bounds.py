@@ -44,10 +44,16 @@ def g(n):
     return n * 2.0 ** -24
 
 
-def bounds_head(q, k, v, do, o_gpu, lse_err, scale, causal, kv_len=None):
+def bounds_head(q, k, v, do, o_gpu, lse_err, scale, causal, kv_len=None, u=U, tiny=2.0 ** -134):
     """Per-element error bounds (dQ, dK, dV) of one head, from the module
-    docstring's derivation. Inputs are fp64 arrays of the bf16 values;
-    lse_err [Nq] is the forward's LSE error (0 on rows with no key)."""
+    docstring's derivation. Inputs are fp64 arrays of the 16-bit values;
+    lse_err [Nq] is the forward's LSE error (0 on rows with no key). u is the
+    unit roundoff of the element type (2^-8 bf16, 2^-11 fp16) and tiny half
+    its subnormal spacing (2^-134 bf16, 2^-25 fp16): a P or dS value below the
+    smallest normal is rounded with that absolute error instead of u
+    relative, which adds tiny * sum |dO| to dV and scale * tiny * sum |K|
+    (|Q|) to dQ (dK)."""
+    U = u
     nq, D = q.shape
     nk = k.shape[0]
     p = orc.softmax_weights(q, k, scale, causal, kv_len)
@@ -61,4 +67,7 @@ def bounds_head(q, k, v, do, o_gpu, lse_err, scale, causal, kv_len=None):
     bv = ((2 * U + g(nq)) * p + eps * p).T @ np.abs(do)
     bq = scale * (((2 * U + g(nk) + eps) * e1 + (1 + 2 * U) * e2) @ np.abs(k))
     bk = scale * (((2 * U + g(nq) + eps) * e1 + (1 + 2 * U) * e2).T @ np.abs(q))
+    bv = bv + tiny * np.abs(do).sum(axis=0)[None, :]
+    bq = bq + scale * tiny * np.abs(k).sum(axis=0)[None, :]
+    bk = bk + scale * tiny * np.abs(q).sum(axis=0)[None, :]
     return 1.01 * bq + ABS, 1.01 * bk + ABS, 1.01 * bv + ABS

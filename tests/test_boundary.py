@@ -37,7 +37,9 @@ def test_header_declares_the_api():
         ["fa_forward", "fa_forward_masked", "fa_forward_f16", "fa_forward_f16_masked",
          "fa_forward_f32", "fa_forward_f32_masked", "fa_rope", "fa_rope_workspace_bytes", "fa_forward_rope",
          "fa_decode_workspace_bytes", "fa_decode_splitkv", "fa_decode_splitkv_masked",
-         "fa_backward_workspace_bytes", "fa_backward", "fa_backward_masked", "fa_status_string"])
+         "fa_decode_splitkv_f16", "fa_decode_splitkv_f16_masked",
+         "fa_backward_workspace_bytes", "fa_backward", "fa_backward_masked", "fa_backward_f16",
+         "fa_backward_f16_masked", "fa_status_string"])
 
 
 def test_every_declared_symbol_is_exported(lib):

@@ -31,6 +31,7 @@ import pytest
 import torch
 
 import synth
+from grad_bounds import bounds_head
 from oracle import attention as orc
 
 pytestmark = pytest.mark.gpu
@@ -181,3 +182,67 @@ def test_forward_rope_equals_rope_then_forward(fa):
     b = fa.fa_forward(fa.fa_rope(q, cos, sin), fa.fa_rope(k, cos, sin), v, causal=1)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+DEC16_CASES = [
+    # (B, H, Nk, D, splits, kv_lens)
+    (4, 8, 5000, 128, 16, None),
+    (3, 4, 777, 64, 64, [700, 0, 64]),
+]
+
+
+@pytest.mark.parametrize("case", DEC16_CASES, ids=lambda c: "x".join(map(str, c[:5])) + f"-{c[5]}")
+def test_fp16_decode(fa, case):
+    B, H, Nk, D, S, kv_lens = case
+    print(f"[case] fp16 decode {case}", flush=True)
+    q, k, v = synth.make_qkv(B, H, 1, Nk, D, torch.float16, seed=55)
+    lens = None if kv_lens is None else torch.tensor(kv_lens, dtype=torch.int32, device=DEV)
+    o, lse = fa.fa_decode_splitkv(q.to(DEV), k.to(DEV), v.to(DEV), S, kv_lens=lens)
+    torch.cuda.synchronize()
+    assert o.dtype == torch.float16
+    ro, rl = orc.decode(f64(q), f64(k), f64(v), 1.0 / math.sqrt(D), kv_lens=kv_lens)
+    check(f"fp16 decode {case}", f64(o)[:, :, 0], f64(lse), ro[:, :, 0], rl[:, :, 0], torch.float16)
+
+
+BWD16_CASES = [
+    # (B, H, Nq, Nk, D, causal, kv_lens, qk_mul)
+    (1, 2, 256, 256, 128, 0, None, 1.0),
+    (1, 2, 300, 300, 64, 1, None, 1.0),
+    (2, 2, 129, 400, 128, 2, [400, 100], 1.0),
+    (1, 2, 513, 513, 128, 1, None, 3.0),
+]
+
+
+@pytest.mark.parametrize("case", BWD16_CASES, ids=lambda c: "x".join(map(str, c[:6])) + f"-{c[6]}-{c[7]}")
+def test_fp16_backward(fa, case):
+    """fp16 gradients within the bounds of tests/grad_bounds.py with fp16's
+    unit roundoff 2^-11 and subnormal half-spacing 2^-25."""
+    B, H, Nq, Nk, D, causal, kv_lens, mul = case
+    print(f"[case] fp16 bwd {case}", flush=True)
+    q, k, v = synth.make_qkv(B, H, Nq, Nk, D, torch.float16, seed=56, qk_mul=mul)
+    do = synth.make_do(B, H, Nq, D, torch.float16, seed=56)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    lens = None if kv_lens is None else torch.tensor(kv_lens, dtype=torch.int32, device=DEV)
+    o, lse = fa.fa_forward_f16(qd, kd, vd, causal=causal, kv_lens=lens)
+    dq, dk, dv = fa.fa_backward(qd, kd, vd, o, dod, lse, causal=causal, kv_lens=lens)
+    torch.cuda.synchronize()
+    assert dq.dtype == torch.float16
+    qn, kn, vn, don = f64(q), f64(k), f64(v), f64(do)
+    on, ln, got = f64(o), f64(lse), (f64(dq), f64(dk), f64(dv))
+    scale = 1.0 / math.sqrt(D)
+    rl = orc.attention(qn, kn, vn, scale, causal, kv_lens=kv_lens)[1]
+    worst = 0.0
+    for b in range(B):
+        L = Nk if kv_lens is None else kv_lens[b]
+        ref = orc.attention_backward(qn[b:b + 1], kn[b:b + 1], vn[b:b + 1], don[b:b + 1], scale, causal,
+                                     kv_lens=[L])
+        for h in range(H):
+            empty = np.isneginf(rl[b, h])
+            lse_err = np.where(empty, 0.0, np.abs(np.where(empty, 0.0, ln[b, h]) - np.where(empty, 0.0, rl[b, h])))
+            bounds = bounds_head(qn[b, h], kn[b, h], vn[b, h], don[b, h], on[b, h], lse_err, scale, causal, L,
+                                 u=2.0 ** -11, tiny=2.0 ** -25)
+            for name, g, r, bd in zip(("dq", "dk", "dv"), got, ref, bounds):
+                ratio = np.abs(g[b, h] - r[0, h]) / bd
+                worst = max(worst, float(ratio.max()))
+                assert np.isfinite(g[b, h]).all() and ratio.max() <= 1.0, f"{case} {name} ({b},{h}) {ratio.max():.3f}"
+    print(f"[f16/rope] fp16 bwd {case}: worst err/bound {worst:.3f}", flush=True)
