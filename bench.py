@@ -254,14 +254,15 @@ def main():
         bms = time_steps(bstep, args.backward_steps, args.warmup, torch)
         fwd_flops, _ = workload_counts(bw)
         btf = 2.5 * fwd_flops / (bms * 1e-3) / 1e12
+        bdigest = kernel_source_digest(["fa_bwd.hip", "fa_device.h", "fa_internal.h"])
         result["backward"] = {
             "workload": bw.name, "ms_per_call": round(bms, 6), "value": round(btf, 3), "unit": "TFLOP/s",
             "algorithmic_flops": 2.5 * fwd_flops,
             "roofline": {"kernel": "bwd_rowdot_kernel + bwd_dq_kernel + bwd_dkdv_kernel", "bound": "mfma",
                          "achieved": round(btf, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(btf / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                         "kernel_source_digest": kernel_source_digest(["fa_bwd.hip", "fa_device.h",
-                                                                       "fa_internal.h"])},
+                         "frac": round(btf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": measured_traffic(f"bwd_kernels_{bw.name}", bdigest),
+                         "kernel_source_digest": bdigest},
         }
         del bq, bk, bv, bdo, bo, grads, bws
 
