@@ -427,15 +427,18 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     const int my_first = first_tile(kw0);
 
     // L and D of tile u through registers of wave 0 (lanes 0-31: L, 32-63: D).
+    // The load is issued with the tile's DMA and its value first used after
+    // the next tile's compute, when it is scaled and written to LDS, so the
+    // global-load latency stays off the critical path.
     float ld_reg = 0.f;
     auto fetch_ld = [&](int u) __attribute__((always_inline)) {
         if (wave == 0) {
             const int q = min(u * kBT + j, Nq - 1);
-            ld_reg = h == 0 ? L[q] * kLog2e : Dv[q];
+            ld_reg = h == 0 ? L[q] : Dv[q];
         }
     };
     auto put_ld = [&](int buf) __attribute__((always_inline)) {
-        if (wave == 0) ld_lds[buf][lane] = ld_reg;
+        if (wave == 0) ld_lds[buf][lane] = h == 0 ? ld_reg * kLog2e : ld_reg;
     };
     auto stage = [&](int u, uint16_t* qd, uint16_t* od) __attribute__((always_inline)) {
         const int q0 = u * kBT;
