@@ -32,16 +32,16 @@
 //     barriers; the two wave groups (waves 0-3 and 4-7, one of each per SIMD)
 //     run a step apart, so on every SIMD one wave feeds the matrix core while
 //     the other runs the exponentials on the VALU.
-//   * K and V tiles go from global memory straight into LDS
-//     (global_load_lds_dwordx4: no VGPR staging), two tiles deep. Both are
+//   * K and V tiles go from global memory straight into LDS (buffer_load_dwordx4
+//     with the lds bit: no VGPR staging), two tiles deep. Both are
 //     row-major in LDS with an XOR swizzle of their 16-byte chunks chosen so
 //     the MFMA operand reads are free of bank conflicts. The V^T operand (8
 //     consecutive keys of one column per lane) is read with ds_read_b64_tr_b16,
 //     the LDS transpose read: within each 16-lane block, source lane s points
 //     at 4 consecutive columns of key k0 + s/4, and lane i receives column i
-//     of those 4 keys. Rows past Nk are clamped to the last key instead of
-//     branching: they are masked out of S, and their (finite) values are
-//     multiplied by P = 0.
+//     of those 4 keys. The buffer resource of a tile spans only its real keys,
+//     so rows past Lk are out of range and arrive in LDS as zeros: they are
+//     masked out of S, and P = 0 meets a zero V row.
 //   * Conditional rescaling (the FA4 refinement the iThome article describes
 //     after the alpha derivation): the running maximum of a wave's rows is
 //     only moved, and O and l rescaled, when some row's tile maximum exceeds it
@@ -97,6 +97,22 @@ __device__ __forceinline__ int v_swz(int key) {
 
 #define LDS_AS __attribute__((address_space(3)))
 
+// Word 3 of a raw buffer resource on gfx9-family parts: 32-bit data format,
+// no swizzle, no index stride.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+// Slots I .. N-1 of a wave's share of a tile load: slot I is 16 bytes per
+// lane, 1 KB above slot I-1 in LDS. The immediate offset supplies that step
+// and moves the memory address by the same amount.
+template <int N, int I = 0>
+__device__ __forceinline__ void buffer_lds_slots(__amdgpu_buffer_rsrc_t rsrc, LDS_AS void* base,
+                                                 const uint32_t* voff) {
+    if constexpr (I < N) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, base, 16, voff[I], 0, I * 1024, 0);
+        buffer_lds_slots<N, I + 1>(rsrc, base, voff);
+    }
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(kFwdThreads, 1)
 void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
@@ -117,9 +133,14 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     constexpr int NDB = D / 32;                // 32-wide d blocks of O^T
     constexpr int NPV = BN / 16;               // 16-key steps of the PV MFMA
     constexpr int CPR = D / 8;                 // 16-byte chunks per row
-    constexpr int kLoadWaves = kFwdWaves / 2;     // group 0 issues every tile load
+    constexpr int kLoadWaves = kFwdWaves / 2;     // one group's waves share a tile load
     constexpr int NLD = BN * CPR / (64 * kLoadWaves);   // DMA chunks per thread per tensor
     static_assert(NLD * 64 * kLoadWaves == BN * CPR, "loader covers the tile");
+    // Who loads tiles, and when (both measured): with D = 128, group 0 loads K
+    // and group 1 loads V, each at the start of its softmax step; with
+    // D = 64, whose softmax step has twice the exponentials per tile, group 0
+    // loads both right after its MFMA step.
+    constexpr bool kSplitLoads = D == 128;
 
     // Two K and two V tile buffers. Four distinct arrays, selected statically
     // (the phase loop below is unrolled over two tiles), let the compiler see
@@ -207,28 +228,27 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     const int wlast = wrow0 + 31 + off;        // last key the wave's last row may see
     const int my_tiles = CAUSAL ? (wlast < 0 ? 0 : min(ntiles, wlast / BN + 1)) : ntiles;
 
-    // DMA slots (group 0 only): chunk p = (i*4 + wave)*64 + lane of a tile
-    // lands at byte 16*p of the LDS tile and holds logical chunk
-    // (p % CPR) ^ swz(row).
-    const int lwave = wave & (kLoadWaves - 1);
-    int ld_row[NLD], ld_kcol[NLD], ld_vcol[NLD];
+    // Tile load slots: chunk p = (lwave*NLD + i)*64 + lane of a tile lands at
+    // byte 16*p of the LDS tile and holds logical chunk (p % CPR) ^ swz(row)
+    // of row p / CPR. The per-lane memory offsets are stored net of slot i's
+    // immediate offset (i KB).
+    const int lwave = __builtin_amdgcn_readfirstlane(wave & (kLoadWaves - 1));
+    uint32_t ld_koff[NLD], ld_voff[NLD];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-        const int p = (i * kLoadWaves + lwave) * 64 + lane;
-        ld_row[i] = p / CPR;
-        ld_kcol[i] = ((p % CPR) ^ k_swz<CPR>(ld_row[i])) * 8;
-        ld_vcol[i] = ((p % CPR) ^ v_swz<CPR>(ld_row[i])) * 8;
+        const int p = (lwave * NLD + i) * 64 + lane;
+        const int row = p / CPR;
+        ld_koff[i] = (uint32_t)(row * D + ((p % CPR) ^ k_swz<CPR>(row)) * 8) * 2 - i * 1024;
+        ld_voff[i] = (uint32_t)(row * D + ((p % CPR) ^ v_swz<CPR>(row)) * 8) * 2 - i * 1024;
     }
-    auto dma = [&](const uint16_t* src, const int* col, int kv0, uint16_t* dst) __attribute__((always_inline)) {
-        const int last = Lk - 1 - kv0;           // >= 0: only tiles below kend <= Lk are loaded
-        const uint16_t* base = src + (size_t)kv0 * D;
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            const int row = min(ld_row[i], last);
-            __builtin_amdgcn_global_load_lds((const void*)(base + (uint32_t)(row * D + col[i])),
-                                             (LDS_AS void*)(LDS_AS uint16_t*)(dst + (i * kLoadWaves + lwave) * 512),
-                                             16, 0, 0);
-        }
+    // One tensor's tile at key kv0. The resource spans the tile's real keys
+    // only, so every address is a per-lane constant and only the resource base
+    // moves from tile to tile (scalar arithmetic).
+    auto dma = [&](const uint16_t* src, const uint32_t* voff, int kv0, uint16_t* dst) __attribute__((always_inline)) {
+        const int rows = min(Lk - kv0, BN);      // > 0: only tiles below kend <= Lk are loaded
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(src + (size_t)kv0 * D), (short)0, rows * D * 2, kBufferRsrcWord3);
+        buffer_lds_slots<NLD>(rsrc, (LDS_AS void*)(LDS_AS uint16_t*)(dst + lwave * NLD * 512), voff);
     };
 
     f32x16_t acc_o[NDB];
@@ -389,11 +409,19 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     // one extra barrier first (and group 0 one at the end): barriers match by
     // count, so group 1 always runs one step behind group 0 and, on every SIMD,
     // one wave feeds the matrix core while the other does softmax.
-    // Tile buffers: K(t) in k_lds[t%2], V(t) in v_lds[t%2]. Group 0 issues the
-    // DMA of K(t+1) and V(t) at the start of its M(t) and waits for it at the
-    // end of its S(t): the next barrier publishes it, one step before group 0
-    // and two before group 1 first read it, and after the last read (group 1's
-    // M(t-1)) of the buffers it overwrites.
+    // Tile buffers: K(t) in k_lds[t%2], V(t) in v_lds[t%2]. Every load is
+    // waited for at the end of the issuing wave's S step, and the barrier after
+    // it publishes the tile.
+    //   * Split loads (D = 128): group 0 loads K(t+1) during its S(t), which
+    //     runs beside group 1's M(t) (reading K(t), V(t-1)); the buffer's last
+    //     reader was group 1's M(t-1), and the first reader is group 0's
+    //     M(t+1). Group 1 loads V(t+1) during its S(t), which runs beside group
+    //     0's M(t+1) (reading K(t+1), V(t)); both groups last read the buffer
+    //     (as V(t-1)) in their M(t), and group 0's M(t+2) reads it first.
+    //     K(0) and V(0) are loaded before the loop.
+    //   * Group-0 loads (D = 64): group 0 loads K(t+1) and V(t) right after its
+    //     M(t); group 1's M(t-1), the last reader of both buffers, is over, and
+    //     group 0's M(t+1) is the first reader.
     // Wave-uniform by construction; readfirstlane makes that visible, so the
     // conditional barriers below are scalar branches.
     const bool loader = __builtin_amdgcn_readfirstlane(group) == 0;
@@ -402,18 +430,22 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     // without the memory fence of __syncthreads, which would otherwise wait
     // for the tile DMA still in flight. The barrier after the S step publishes
     // the DMA that the loader waves have just waited for.
-    auto tile_steps = [&](int t, const uint16_t* kb, const uint16_t* vb_prev, uint16_t* kb_next,
+    auto tile_steps = [&](int t, const uint16_t* kb, uint16_t* vb_prev, uint16_t* kb_next,
                           uint16_t* vb_cur) __attribute__((always_inline)) {
         step_mfma(t, kb, vb_prev);
-        if (loader && t < ntiles) {
-            if (t + 1 < ntiles) dma(K, ld_kcol, (t + 1) * BN, kb_next);
-            dma(V, ld_vcol, t * BN, vb_cur);
+        if (!kSplitLoads && loader && t < ntiles) {
+            if (t + 1 < ntiles) dma(K, ld_koff, (t + 1) * BN, kb_next);
+            dma(V, ld_voff, t * BN, vb_cur);
         }
         // sched_barrier(0): no instruction moves across the step boundary, so
         // the two steps keep their own (smaller) sets of live registers.
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
+        if (kSplitLoads && t + 1 < ntiles) {
+            if (loader) dma(K, ld_koff, (t + 1) * BN, kb_next);
+            else dma(V, ld_voff, (t + 1) * BN, vb_prev);
+        }
         step_softmax(t);
         // vmcnt(0) on every wave (a no-op for waves with no DMA in flight), so
         // the compiler knows no tile DMA is pending past this point.
@@ -423,7 +455,10 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    if (loader && ntiles > 0) dma(K, ld_kcol, 0, k_lds0);
+    if (ntiles > 0) {
+        if (loader) dma(K, ld_koff, 0, k_lds0);
+        else if (kSplitLoads) dma(V, ld_voff, 0, v_lds0);
+    }
     __builtin_amdgcn_s_waitcnt(0xF70);
     __syncthreads();
     if (!loader) __builtin_amdgcn_s_barrier();
