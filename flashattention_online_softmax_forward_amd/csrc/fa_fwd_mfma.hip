@@ -348,13 +348,16 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
         const bool diag = CAUSAL && (kv0 + BN - 1 > wrow0 + off);
         if (ragged || diag) {
 #pragma unroll
-            for (int c = 0; c < NCB; ++c)
+            for (int c = 0; c < NCB; ++c) {
+                // Keys from lim on are dead for this row: past Lk, or (causal)
+                // past qrow + off. Against the offset of key (c, r) within the
+                // lane's keys that is one compare with a small constant.
+                const int lim = CAUSAL ? min(Lk, qrow + off + 1) : Lk;
+                const int rel = lim - (kv0 + c * 32 + h * 8);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kv0 + c * 32 + (r >> 3) * 16 + h * 8 + (r & 7);
-                    const bool dead = key >= Lk || (CAUSAL && key > qrow + off);
-                    if (dead) s[c][r] = -INFINITY;
-                }
+                for (int r = 0; r < 16; ++r)
+                    if ((r >> 3) * 16 + (r & 7) >= rel) s[c][r] = -INFINITY;
+            }
         }
         // Row max and row sum as several independent chains (a single chain
         // of dependent max / add instructions would leave the VALU waiting on
