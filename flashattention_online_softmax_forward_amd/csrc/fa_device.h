@@ -112,12 +112,17 @@ __device__ __forceinline__ void rope_pair_chunk(uint32_t* x, const float* c, con
 // Hardware base-2 exponential (v_exp_f32); exp2(-inf) = 0.
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// NaN-propagating maximum (IEEE 754-2019 maximum). gfx950 has it as
+// v_maximum3_f32, which needs no quieting of its operands, where fmaxf's
+// number-preferring maxnum costs a canonicalising v_max per raw MFMA result.
+__device__ __forceinline__ float fmax_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Combine a value with the one held by lane (lane ^ 32): v_permlane32_swap
 // returns both halves, so a symmetric op of the two results is the same in
 // every lane.
 __device__ __forceinline__ float max_xor32(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return fmax_nan(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float sum_xor32(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -369,8 +369,8 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
 #pragma unroll
         for (int c = 0; c < NCB; ++c)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mxc[r % NCH] = fmaxf(mxc[r % NCH], s[c][r]);
-        const float m_tile = max_xor32(fmaxf(fmaxf(mxc[0], mxc[1]), fmaxf(mxc[2], mxc[3]))) * scale2;
+            for (int r = 0; r < 16; ++r) mxc[r % NCH] = fmax_nan(mxc[r % NCH], s[c][r]);
+        const float m_tile = max_xor32(fmax_nan(fmax_nan(mxc[0], mxc[1]), fmax_nan(mxc[2], mxc[3]))) * scale2;
         // Move the maximum (and rescale O, l) only when some row of the wave
         // outgrew it by more than the threshold.
         if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleThreshold)) {
@@ -383,7 +383,7 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
         }
-        float lsc[NCH] = {0.f, 0.f, 0.f, 0.f};
+        float lsc[NCH];            // chains start from the tile's first values (no 0 + p)
 #pragma unroll
         for (int c = 0; c < NCB; ++c)
 #pragma unroll
@@ -392,7 +392,7 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     p[e] = exp2_hw(__builtin_fmaf(s[c][u * 8 + e], scale2, -m_run));
-                    lsc[e % NCH] += p[e];
+                    lsc[e % NCH] = (c == 0 && u == 0 && e < NCH) ? p[e] : lsc[e % NCH] + p[e];
                 }
                 u32x4_t w;
                 w[0] = E::pack2(p[0], p[1]);
