@@ -12,8 +12,8 @@
 //   * bf16 or fp16 inputs (Elem<T>: MFMA, transpose read, packing).
 //   * Both product kernels use v_mfma_f32_32x32x16_bf16 (_f16) with 4 waves x 32
 //     rows per workgroup and stream the other operand through LDS in tiles of
-//     32 rows (global_load_lds_dwordx4 DMA, double-buffered, one barrier per
-//     tile).
+//     32 rows (buffer_load_dwordx4 straight to LDS, double-buffered, one
+//     barrier per tile).
 //   * dQ: a wave owns 32 query rows; Q and dO stay in VGPRs as B operands.
 //     S^T = K Q^T and dP^T = V dO^T put one query per lane, so L and D are
 //     per-lane scalars. The rows of K and V fed to the A operand are permuted
@@ -32,7 +32,7 @@
 //   * Masking: causal (key j visible from query i iff j <= i + off, off = 0
 //     top-left or Lk - Nq bottom-right), padding keys (past the batch entry's
 //     real key count Lk) and queries past Nq get P = 0 (so dS = 0 too); rows
-//     past the end are loaded clamped to the last row and never stored. A
+//     past the end are staged as zeros and never stored. A
 //     query row with no visible key (LSE = -inf) only ever meets masked pairs,
 //     so its P is forced to 0 before exp2(+inf) can be used; its dQ is 0.
 //   * dQ, dK, dV are accumulated in fp32 and rounded to bf16 once.
@@ -67,38 +67,44 @@ __device__ __forceinline__ int swz(int row) {
                      : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
 }
 
-// One global_load_lds_dwordx4: every lane copies 16 bytes from base + voff to
-// LDS address lds + 16 * lane (lds is wave-uniform, in M0). Inline asm keeps
-// it out of the compiler's wait-count bookkeeping; the kernels wait for their
-// loads themselves before the barrier that publishes them.
-__device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
-}
 __device__ __forceinline__ void lds_dma_wait_all() {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
-__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
-    return (uint32_t)(uintptr_t)(LDS_AS const uint16_t*)p;
-}
 
-// Stage `rows` rows (a multiple of 32) of a row-major [*, D] bf16 array into
-// LDS with the chunk swizzle: chunk p of the tile lands at byte 16*p and holds
-// logical chunk (p % CPR) ^ swz(row) of row p / CPR. Rows past `last` (the
-// last valid row, relative to src) are clamped to it.
-template <int D>
-__device__ __forceinline__ void stage_rows(const uint16_t* src, int rows, int last, uint16_t* dst,
-                                           int wave, int lane) {
-    constexpr int CPR = D / 8;
-    const int per = rows * CPR / kBwdThreads;          // chunks per thread
-    for (int i = 0; i < per; ++i) {
-        const int p = (i * kBwdWaves + wave) * 64 + lane;
-        const int row = p / CPR;
-        const int rr = row < last ? row : last;
-        const uint32_t off = (uint32_t)(rr * D + ((p % CPR) ^ swz<CPR>(row)) * 8) * 2u;
-        lds_dma16(src, off, lds_addr(dst + (i * kBwdWaves + wave) * 512));
+// Staging of ROWS rows of a row-major [*, D] 16-bit array into LDS with the
+// chunk swizzle: chunk p of the tile lands at byte 16*p and holds logical
+// chunk (p % CPR) ^ swz(row) of row p / CPR. Wave w moves chunks
+// (w*PER + i)*64 + lane, i < PER, with buffer loads straight to LDS; the
+// per-lane offsets are computed once, and a tile's resource spans only its
+// valid rows, so rows past them arrive as zeros (always masked).
+template <int D, int ROWS>
+struct StageSlots {
+    static constexpr int CPR = D / 8;
+    static constexpr int PER = ROWS * CPR / kBwdThreads;   // chunks per lane
+    static_assert(PER * kBwdThreads == ROWS * CPR, "whole chunks per lane");
+    uint32_t voff[PER];        // memory byte offsets, net of the slot's immediate offset
+    __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int p = (wave * PER + i) * 64 + lane;
+            const int row = p / CPR;
+            voff[i] = (uint32_t)(row * D + ((p % CPR) ^ swz<CPR>(row)) * 8) * 2u - (i % 4) * 1024u;
+        }
     }
-}
+    // Rows [valid, ROWS) of src (0 <= valid <= ROWS) are not read.
+    __device__ __forceinline__ void stage(const uint16_t* src, int valid, uint16_t* dst, int wave) const {
+        const __amdgpu_buffer_rsrc_t rsrc =
+            __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, valid * D * 2, kBufferRsrcWord3);
+        static_assert(PER <= 4 || PER % 4 == 0, "slots go in groups of up to 4");
+        if constexpr (PER <= 4) {
+            buffer_lds_slots<PER>(rsrc, (LDS_AS void*)(LDS_AS uint16_t*)(dst + wave * PER * 512), voff);
+        } else {
+#pragma unroll
+            for (int g = 0; g < PER; g += 4)
+                buffer_lds_slots<4>(rsrc, (LDS_AS void*)(LDS_AS uint16_t*)(dst + (wave * PER + g) * 512), voff + g);
+        }
+    }
+};
 
 // Lane-dependent LDS byte offsets of the MFMA operand reads of a staged
 // 32-row tile. They are the same for every tile buffer (the buffer's base is
@@ -285,10 +291,13 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
     const int wlast = wrow0 + 31 + doff;        // last key the wave's last row may see
     const int my_tiles = CAUSAL ? (wlast < 0 ? 0 : min(ntiles, wlast / kBT + 1)) : ntiles;
 
+    StageSlots<D, kBT> slots;                  // K and V tiles share the offsets
+    slots.init(wave, lane);
     auto stage = [&](int t, uint16_t* kd, uint16_t* vd) __attribute__((always_inline)) {
-        const int kv0 = t * kBT;               // < kend <= Lk, so the clamp row is real
-        stage_rows<D>(K + (size_t)kv0 * D, kBT, Lk - 1 - kv0, kd, wave, lane);
-        stage_rows<D>(V + (size_t)kv0 * D, kBT, Lk - 1 - kv0, vd, wave, lane);
+        const int kv0 = t * kBT;               // < kend <= Lk
+        const int valid = min(Lk - kv0, kBT);
+        slots.stage(K + (size_t)kv0 * D, valid, kd, wave);
+        slots.stage(V + (size_t)kv0 * D, valid, vd, wave);
     };
     auto compute = [&](int t, const uint16_t* kt, const uint16_t* vt) __attribute__((always_inline)) {
         // S^T = K Q^T and dP^T = V dO^T for 32 keys x this wave's 32 queries.
@@ -440,10 +449,13 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     auto put_ld = [&](int buf) __attribute__((always_inline)) {
         if (wave == 0) ld_lds[buf][lane] = h == 0 ? ld_reg * kLog2e : ld_reg;
     };
+    StageSlots<D, kBT> slots;                  // Q and dO tiles share the offsets
+    slots.init(wave, lane);
     auto stage = [&](int u, uint16_t* qd, uint16_t* od) __attribute__((always_inline)) {
-        const int q0 = u * kBT;
-        stage_rows<D>(Q + (size_t)q0 * D, kBT, Nq - 1 - q0, qd, wave, lane);
-        stage_rows<D>(dO + (size_t)q0 * D, kBT, Nq - 1 - q0, od, wave, lane);
+        const int q0 = u * kBT;                // < Nq
+        const int valid = min(Nq - q0, kBT);
+        slots.stage(Q + (size_t)q0 * D, valid, qd, wave);
+        slots.stage(dO + (size_t)q0 * D, valid, od, wave);
     };
     auto v_operand = [&](int kk) __attribute__((always_inline)) {
         return *(LDS_AS const V8*)((LDS_AS const char*)(LDS_AS const uint16_t*)v_blk + voff[kk]);
@@ -516,8 +528,12 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
                                    });
     };
 
-    // Prologue: the block's V rows (clamped to the last key) and the first tile.
-    stage_rows<D>(Vg + ((size_t)bh * Nk + k0) * D, BM_BWD, Nk - 1 - k0, v_blk, wave, lane);
+    // Prologue: the block's V rows (zeros past Nk) and the first tile.
+    {
+        StageSlots<D, BM_BWD> vslots;
+        vslots.init(wave, lane);
+        vslots.stage(Vg + ((size_t)bh * Nk + k0) * D, min(Nk - k0, BM_BWD), v_blk, wave);
+    }
     if (first < nqt) {
         stage(first, q_lds0, o_lds0);
         fetch_ld(first);

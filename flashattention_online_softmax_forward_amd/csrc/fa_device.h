@@ -112,6 +112,26 @@ __device__ __forceinline__ void rope_pair_chunk(uint32_t* x, const float* c, con
 // Hardware base-2 exponential (v_exp_f32); exp2(-inf) = 0.
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Word 3 of a raw buffer resource on gfx9-family parts: 32-bit data format,
+// no swizzle, no index stride.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+// Slots I .. N-1 (N <= 4) of a wave's share of a tile load into LDS
+// (buffer_load_dwordx4 with the lds bit): slot I moves 16 bytes per lane from
+// the resource at voff[I] + 1 KB * I to base + 1 KB * I + 16 * lane. The
+// immediate offset supplies the 1 KB step (it moves the LDS destination and
+// the memory address alike), so voff[I] is stored net of it. A lane whose
+// offset is past the resource's size writes zeros.
+template <int N, int I = 0>
+__device__ __forceinline__ void buffer_lds_slots(__amdgpu_buffer_rsrc_t rsrc, __attribute__((address_space(3))) void* base,
+                                                 const uint32_t* voff) {
+    static_assert(N <= 4, "the immediate offset field holds at most 3 KB");
+    if constexpr (I < N) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, base, 16, voff[I], 0, I * 1024, 0);
+        buffer_lds_slots<N, I + 1>(rsrc, base, voff);
+    }
+}
+
 // NaN-propagating maximum (IEEE 754-2019 maximum). gfx950 has it as
 // v_maximum3_f32, which needs no quieting of its operands, where fmaxf's
 // number-preferring maxnum costs a canonicalising v_max per raw MFMA result.

@@ -97,22 +97,6 @@ __device__ __forceinline__ int v_swz(int key) {
 
 #define LDS_AS __attribute__((address_space(3)))
 
-// Word 3 of a raw buffer resource on gfx9-family parts: 32-bit data format,
-// no swizzle, no index stride.
-constexpr int kBufferRsrcWord3 = 0x00020000;
-
-// Slots I .. N-1 of a wave's share of a tile load: slot I is 16 bytes per
-// lane, 1 KB above slot I-1 in LDS. The immediate offset supplies that step
-// and moves the memory address by the same amount.
-template <int N, int I = 0>
-__device__ __forceinline__ void buffer_lds_slots(__amdgpu_buffer_rsrc_t rsrc, LDS_AS void* base,
-                                                 const uint32_t* voff) {
-    if constexpr (I < N) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, base, 16, voff[I], 0, I * 1024, 0);
-        buffer_lds_slots<N, I + 1>(rsrc, base, voff);
-    }
-}
-
 template <typename T, int D>
 __global__ __launch_bounds__(kFwdThreads, 1)
 void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
