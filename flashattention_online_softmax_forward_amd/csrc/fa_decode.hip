@@ -27,7 +27,7 @@
 
 namespace fa {
 
-constexpr int kDecThreads = 256;
+constexpr int kDecThreads = 1024;    // 16 waves: more loads in flight per chunk (measured +4% over 256)
 constexpr int kDecUnroll = 4;
 
 template <typename T, int D>
