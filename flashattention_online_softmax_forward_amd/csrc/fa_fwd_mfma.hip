@@ -461,22 +461,46 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     // Epilogue: O / l to bf16, LSE = (m + log2 l) * ln 2; a row that saw no
     // key (l = 0, O = 0) gets O = 0 and LSE = -inf.
     const float l_tot = sum_xor32(l_run);
-    if (qrow < Nq) {
-        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-        uint16_t* orow = Og + ((size_t)bh * Nq + qrow) * D;
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    // O goes out through LDS so that every store writes whole rows: the
+    // wave's 32 rows (bf16) are staged in a region of the now idle K/V
+    // buffers (the last barrier above ended every read of them), 16-byte
+    // chunks swizzled by row, then read back four rows per instruction.
+    {
+        constexpr int RB = 32 * D;             // elements of one wave's staged rows
+        static_assert(2 * RB <= TILE, "two waves' rows per tile buffer");
+        const int sb = wave >> 1;              // waves 2b, 2b+1 share tile buffer b
+        uint16_t* ost = (sb == 0 ? k_lds0 : sb == 1 ? k_lds1 : sb == 2 ? v_lds0 : v_lds1) + (wave & 1) * RB;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int a4 = 0; a4 < 4; ++a4) {
-                const int d = db * 32 + a4 * 8 + h * 4;
+                const int c = db * 4 + a4;     // 16-byte chunk of the row: d = 8c .. 8c + 7
                 u32x2_t w;
                 w[0] = E::pack2(acc_o[db][a4 * 4 + 0] * inv, acc_o[db][a4 * 4 + 1] * inv);
                 w[1] = E::pack2(acc_o[db][a4 * 4 + 2] * inv, acc_o[db][a4 * 4 + 3] * inv);
-                *(u32x2_t*)(orow + d) = w;
+                *(LDS_AS u32x2_t*)(LDS_AS uint16_t*)(ost + j * D + (c ^ (j & (CPR - 1))) * 8 + h * 4) = w;
             }
-        if (h == 0 && LSEg)
-            LSEg[(size_t)bh * Nq + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+        // The reads below take other lanes' writes: one wave's LDS
+        // operations complete in order once issued, and the fence keeps the
+        // compiler from moving the reads ahead.
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        constexpr int RPI = 64 / CPR;          // rows per read instruction
+        constexpr int NIT = 32 / RPI;
+        const int c = lane % CPR;
+        u32x4_t w[NIT];
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int r = it * RPI + lane / CPR;
+            w[it] = *(LDS_AS const u32x4_t*)(LDS_AS const uint16_t*)(ost + r * D + (c ^ (r & (CPR - 1))) * 8);
+        }
+        uint16_t* orow = Og + ((size_t)bh * Nq + wrow0 + lane / CPR) * D + c * 8;
+#pragma unroll
+        for (int it = 0; it < NIT; ++it)
+            if (wrow0 + it * RPI + lane / CPR < Nq) *(u32x4_t*)(orow + it * RPI * D) = w[it];
     }
+    if (qrow < Nq && h == 0 && LSEg)
+        LSEg[(size_t)bh * Nq + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 template <typename T, int D>
