@@ -134,6 +134,11 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[TILE];
+    // Row staging: Q rows on the way in, O rows on the way out (32 rows per
+    // wave, 16-byte chunks swizzled by row), so that both move whole rows
+    // between HBM and the CU.
+    constexpr int RB = 32 * D;                 // elements of one wave's rows
+    __shared__ __attribute__((aligned(1024))) uint16_t row_lds[kFwdWaves * RB];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -158,52 +163,31 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     const int wrow0 = q0 + wave * 32;
     const int qrow = wrow0 + j;
 
+    // The wave's Q rows go to LDS with buffer loads (whole rows, four per
+    // load; rows past Nq are out of the resource's range and arrive as zeros);
+    // they are read into registers after the first tile loads below.
+    const int qwave = __builtin_amdgcn_readfirstlane(wave);
+    uint16_t* const qst = row_lds + qwave * RB;
+    {
+        constexpr int NQS = RB / 512;          // 1 KB slots per wave
+        uint32_t qoff[NQS];
+#pragma unroll
+        for (int i = 0; i < NQS; ++i) {
+            const int p = i * 64 + lane;       // chunk of the wave's rows
+            const int row = p / CPR;
+            qoff[i] = (uint32_t)(row * D + ((p % CPR) ^ (row & (CPR - 1))) * 8) * 2 - (i % 4) * 1024;
+        }
+        const int qrows = min(max(Nq - wrow0, 0), 32);
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(Q + (size_t)min(wrow0, Nq) * D), (short)0, qrows * D * 2, kBufferRsrcWord3);
+        static_assert(NQS % 4 == 0, "slots in groups of 4");
+#pragma unroll
+        for (int g = 0; g < NQS; g += 4)
+            buffer_lds_slots<4>(rsrc, (LDS_AS void*)(LDS_AS uint16_t*)(qst + g * 512), qoff + g);
+    }
     // Q as the B operand: lane (j, h) holds row qrow, d = 16*kk + 8*h .. +7.
     u32x4_t qw[NKK];
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-        qw[kk] = u32x4_t{0u, 0u, 0u, 0u};
-        if (qrow < Nq) qw[kk] = *(const u32x4_t*)(Q + (size_t)qrow * D + kk * 16 + h * 8);
-    }
-    // Fused RoPE prologue on Q: the row is rotated in registers, once per
-    // workgroup, at its position (qrow, shifted by the bottom-right offset so
-    // the queries are the newest tokens). Both partners of every rotated pair
-    // are in this lane: d and d + D/2 (rotate-half) are chunks kk and
-    // kk + D/32 of the same half h; adjacent pairs share a chunk.
-    if (rope_cos && qrow < Nq) {
-        const int pos = max(0, qrow + off);
-        const float* cr = rope_cos + (size_t)pos * (D / 2);
-        const float* sr = rope_sin + (size_t)pos * (D / 2);
-        if (rope_style == kRopeHalf) {
-#pragma unroll
-            for (int kk = 0; kk < NKK / 2; ++kk) {
-                const int i0 = kk * 16 + h * 8;
-                const f32x4_t c0 = *(const f32x4_t*)(cr + i0), c1 = *(const f32x4_t*)(cr + i0 + 4);
-                const f32x4_t s0 = *(const f32x4_t*)(sr + i0), s1 = *(const f32x4_t*)(sr + i0 + 4);
-                const float c[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-                const float sn[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-                uint32_t a[4] = {qw[kk][0], qw[kk][1], qw[kk][2], qw[kk][3]};
-                uint32_t b[4] = {qw[kk + NKK / 2][0], qw[kk + NKK / 2][1], qw[kk + NKK / 2][2], qw[kk + NKK / 2][3]};
-                rope_half_chunks<T>(a, b, c, sn);
-                qw[kk] = u32x4_t{a[0], a[1], a[2], a[3]};
-                qw[kk + NKK / 2] = u32x4_t{b[0], b[1], b[2], b[3]};
-            }
-        } else {
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                const int p0 = kk * 8 + h * 4;
-                const f32x4_t c4 = *(const f32x4_t*)(cr + p0), s4 = *(const f32x4_t*)(sr + p0);
-                const float c[4] = {c4[0], c4[1], c4[2], c4[3]};
-                const float sn[4] = {s4[0], s4[1], s4[2], s4[3]};
-                uint32_t x[4] = {qw[kk][0], qw[kk][1], qw[kk][2], qw[kk][3]};
-                rope_pair_chunk<T>(x, c, sn);
-                qw[kk] = u32x4_t{x[0], x[1], x[2], x[3]};
-            }
-        }
-    }
     V8 qf[NKK];
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) qf[kk] = __builtin_bit_cast(V8, qw[kk]);
 
     int kend = Lk;
     if (CAUSAL) kend = max(0, min(Lk, min(q0 + BM_FWD, Nq) + off));
@@ -448,6 +432,48 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     }
     __builtin_amdgcn_s_waitcnt(0xF70);
     __syncthreads();
+    // Q rows from the staging area into the B operand registers.
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+        qw[kk] = *(LDS_AS const u32x4_t*)(LDS_AS const uint16_t*)(qst + j * D + ((kk * 2 + h) ^ (j & (CPR - 1))) * 8);
+    // Fused RoPE prologue on Q: the row is rotated in registers, once per
+    // workgroup, at its position (qrow, shifted by the bottom-right offset so
+    // the queries are the newest tokens). Both partners of every rotated pair
+    // are in this lane: d and d + D/2 (rotate-half) are chunks kk and
+    // kk + D/32 of the same half h; adjacent pairs share a chunk.
+    if (rope_cos && qrow < Nq) {
+        const int pos = max(0, qrow + off);
+        const float* cr = rope_cos + (size_t)pos * (D / 2);
+        const float* sr = rope_sin + (size_t)pos * (D / 2);
+        if (rope_style == kRopeHalf) {
+#pragma unroll
+            for (int kk = 0; kk < NKK / 2; ++kk) {
+                const int i0 = kk * 16 + h * 8;
+                const f32x4_t c0 = *(const f32x4_t*)(cr + i0), c1 = *(const f32x4_t*)(cr + i0 + 4);
+                const f32x4_t s0 = *(const f32x4_t*)(sr + i0), s1 = *(const f32x4_t*)(sr + i0 + 4);
+                const float c[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+                const float sn[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+                uint32_t a[4] = {qw[kk][0], qw[kk][1], qw[kk][2], qw[kk][3]};
+                uint32_t b[4] = {qw[kk + NKK / 2][0], qw[kk + NKK / 2][1], qw[kk + NKK / 2][2], qw[kk + NKK / 2][3]};
+                rope_half_chunks<T>(a, b, c, sn);
+                qw[kk] = u32x4_t{a[0], a[1], a[2], a[3]};
+                qw[kk + NKK / 2] = u32x4_t{b[0], b[1], b[2], b[3]};
+            }
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                const int p0 = kk * 8 + h * 4;
+                const f32x4_t c4 = *(const f32x4_t*)(cr + p0), s4 = *(const f32x4_t*)(sr + p0);
+                const float c[4] = {c4[0], c4[1], c4[2], c4[3]};
+                const float sn[4] = {s4[0], s4[1], s4[2], s4[3]};
+                uint32_t x[4] = {qw[kk][0], qw[kk][1], qw[kk][2], qw[kk][3]};
+                rope_pair_chunk<T>(x, c, sn);
+                qw[kk] = u32x4_t{x[0], x[1], x[2], x[3]};
+            }
+        }
+    }
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) qf[kk] = __builtin_bit_cast(V8, qw[kk]);
     if (!loader) __builtin_amdgcn_s_barrier();
     // Steps M(t), S(t) for t = 0 .. ntiles (M(ntiles) is the last PV product,
     // S(ntiles) is empty); two tiles per iteration keep buffer choice static.
@@ -462,15 +488,10 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     // key (l = 0, O = 0) gets O = 0 and LSE = -inf.
     const float l_tot = sum_xor32(l_run);
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    // O goes out through LDS so that every store writes whole rows: the
-    // wave's 32 rows (bf16) are staged in a region of the now idle K/V
-    // buffers (the last barrier above ended every read of them), 16-byte
-    // chunks swizzled by row, then read back four rows per instruction.
+    // O goes out through the wave's row staging (its Q reads ended before
+    // the key loop) so that every store writes whole rows.
     {
-        constexpr int RB = 32 * D;             // elements of one wave's staged rows
-        static_assert(2 * RB <= TILE, "two waves' rows per tile buffer");
-        const int sb = wave >> 1;              // waves 2b, 2b+1 share tile buffer b
-        uint16_t* ost = (sb == 0 ? k_lds0 : sb == 1 ? k_lds1 : sb == 2 ? v_lds0 : v_lds1) + (wave & 1) * RB;
+        uint16_t* ost = qst;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
