@@ -174,20 +174,44 @@ __device__ __forceinline__ void load_b_rows(const uint16_t* base, int row, bool 
 }
 
 // Store an fp32 accumulator of 32 rows x D held transposed (lane j = row,
-// register r of block db = column 32*db + 8*(r/4) + 4*h + r%4) as bf16,
-// multiplied by `mul`.
+// register r of block db = column 32*db + 8*(r/4) + 4*h + r%4) as 16-bit
+// values multiplied by `mul`, to rows dst[0 .. valid) (row-major [*, D]).
+// The rows go through `stage`, 32*D elements of LDS private to the wave, with
+// their 16-byte chunks swizzled by row, so that every store instruction
+// writes whole rows, 16 bytes per lane.
 template <typename T, int D>
-__device__ __forceinline__ void store_rows(uint16_t* rowp, const f32x16_t* acc, int h, float mul) {
+__device__ __forceinline__ void store_rows_staged(uint16_t* dst, int valid, const f32x16_t* acc, float mul,
+                                                  uint16_t* stage, int lane) {
+    constexpr int CPR = D / 8;
+    const int j = lane & 31, h = lane >> 5;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
-            const int d = db * 32 + a4 * 8 + h * 4;
+            const int c = db * 4 + a4;         // 16-byte chunk: columns 8c .. 8c + 7
             u32x2_t w;
             w[0] = Elem<T>::pack2(acc[db][a4 * 4 + 0] * mul, acc[db][a4 * 4 + 1] * mul);
             w[1] = Elem<T>::pack2(acc[db][a4 * 4 + 2] * mul, acc[db][a4 * 4 + 3] * mul);
-            *(u32x2_t*)(rowp + d) = w;
+            *(LDS_AS u32x2_t*)(LDS_AS uint16_t*)(stage + j * D + (c ^ (j & (CPR - 1))) * 8 + h * 4) = w;
         }
+    // The reads take other lanes' writes: one wave's LDS operations complete
+    // in order once issued, and the fence keeps the compiler from moving the
+    // reads ahead.
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    constexpr int RPI = 64 / CPR;              // rows per store instruction
+    constexpr int NIT = 32 / RPI;
+    const int c = lane % CPR;
+    u32x4_t w[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int r = it * RPI + lane / CPR;
+        w[it] = *(LDS_AS const u32x4_t*)(LDS_AS const uint16_t*)(stage + r * D + (c ^ (r & (CPR - 1))) * 8);
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int r = it * RPI + lane / CPR;
+        if (r < valid) *(u32x4_t*)(dst + (size_t)r * D + c * 8) = w[it];
+    }
 }
 
 // N MFMAs acc[dst(i)] += op(i) x b(i), each A operand read LEAD MFMAs ahead
@@ -355,7 +379,10 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
         __syncthreads();
     }
 
-    if (qvalid) store_rows<T, D>(dQg + ((size_t)bh * Nq + qrow) * D, acc, h, scale);
+    // The last barrier above ended every read of the tile buffers: each wave
+    // stages its dQ rows in one of them.
+    uint16_t* const qst = wave == 0 ? k_lds0 : wave == 1 ? k_lds1 : wave == 2 ? v_lds0 : v_lds1;
+    store_rows_staged<T, D>(dQg + ((size_t)bh * Nq + wrow0) * D, Nq - wrow0, acc, scale, qst, lane);
 }
 
 // dK and dV for 128 keys of one (batch, head), streaming Q, dO, L and D tiles.
@@ -562,10 +589,12 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
         __syncthreads();
     }
 
-    if (kvalid) {
-        store_rows<T, D>(dKg + ((size_t)bh * Nk + krow) * D, adk, h, scale);
-        store_rows<T, D>(dVg + ((size_t)bh * Nk + krow) * D, adv, h, 1.0f);
-    }
+    // The last barrier above ended every read of the Q / dO tiles and of the
+    // V block: each wave stages its dK rows in one tile buffer and its dV rows
+    // in its own quarter of the V block. Rows past Nk are not stored.
+    uint16_t* const kst = wave == 0 ? q_lds0 : wave == 1 ? q_lds1 : wave == 2 ? o_lds0 : o_lds1;
+    store_rows_staged<T, D>(dKg + ((size_t)bh * Nk + kw0) * D, Nk - kw0, adk, scale, kst, lane);
+    store_rows_staged<T, D>(dVg + ((size_t)bh * Nk + kw0) * D, Nk - kw0, adv, 1.0f, v_blk + wave * 32 * D, lane);
 }
 
 template <typename T, int D>
