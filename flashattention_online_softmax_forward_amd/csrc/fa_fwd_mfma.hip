@@ -125,6 +125,11 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     // D = 64, whose softmax step has twice the exponentials per tile, group 0
     // loads both right after its MFMA step.
     constexpr bool kSplitLoads = D == 128;
+    // Where the row maximum of a tile is taken (measured): with D = 64 the
+    // MFMA step computes it, one maximum3 per PV MFMA after running QK(t)
+    // first, which takes VALU work off the heavier softmax step (+2-3%); with
+    // D = 128 the two steps are balanced and the softmax step keeps it.
+    constexpr bool kMaxInMfma = D == 64;
 
     // Two K and two V tile buffers. Four distinct arrays, selected statically
     // (the phase loop below is unrolled over two tiles), let the compiler see
@@ -263,11 +268,24 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
         const int row = c * 32 + srow;
         return *(const V8*)(kb + row * D + (((kk * 2 + h) ^ k_swz<CPR>(row)) * 8));
     };
+    // Scaled row maximum of tile t's scores (NaN-propagating).
+    auto tile_max = [&]() __attribute__((always_inline)) {
+        constexpr int NCH = 4;
+        float mxc[NCH];
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) mxc[k] = s[0][k];
+#pragma unroll
+        for (int c = 0; c < NCB; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mxc[r % NCH] = fmax_nan(mxc[r % NCH], s[c][r]);
+        return max_xor32(fmax_nan(fmax_nan(mxc[0], mxc[1]), fmax_nan(mxc[2], mxc[3]))) * scale2;
+    };
+    float m_pre = kNoKeyMax;   // tile maximum taken by the MFMA step (kMaxInMfma)
     auto step_mfma = [&](int t, const uint16_t* kb, const uint16_t* vb_prev) __attribute__((always_inline)) {
         __builtin_amdgcn_s_setprio(1);
         const bool do_pv = t >= 1 && t - 1 < my_tiles;
         const bool do_qk = t < my_tiles;
-        if (do_pv && do_qk) {
+        if (do_pv && do_qk && !kMaxInMfma) {
             // PV(t-1) then QK(t) as one stream of 2*16 MFMAs, each operand read
             // LEAD MFMAs ahead of its use.
             constexpr int NM = NPVM + NSM;
@@ -293,6 +311,57 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
                 if (nx < NPVM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
                 else if (nx < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
+        } else if (do_pv && do_qk) {
+            // QK(t) then PV(t-1); the row maximum of tile t runs on the VALU
+            // beside the PV MFMAs. The last 4 scores start 4 chains, the
+            // others join EPS per PV MFMA from the second one on (the QK
+            // results are complete by then).
+            constexpr int NM = NPVM + NSM;
+            auto operand = [&](int i) __attribute__((always_inline)) {
+                return i < NSM ? qk_operand(kb, i) : pv_operand(vb_prev, i - NSM);
+            };
+            const f32x16_t zero = {};
+            constexpr int NEL = NCB * 16;
+            constexpr int EPS = (NEL - 4 + NPVM - 2) / (NPVM - 1);
+            constexpr int NMX = (NEL - 4 + EPS - 1) / EPS;
+            static_assert(NMX <= NPVM - 1, "the maximum fits beside the PV MFMAs");
+            float mxc[4];
+            V8 ring[LEAD];
+#pragma unroll
+            for (int i = 0; i < LEAD; ++i) ring[i] = operand(i);
+            __builtin_amdgcn_sched_group_barrier(0x100, LEAD, 0);
+#pragma unroll
+            for (int i = 0; i < NM; ++i) {
+                const V8 a = ring[i % LEAD];
+                if (i + LEAD < NM) ring[i % LEAD] = operand(i + LEAD);
+                if (i < NSM)  // the first d step of each key block starts from zero
+                    s[i % NCB] = E::mfma(a, qf[i / NCB], i < NCB ? zero : s[i % NCB]);
+                else
+                    acc_o[(i - NSM) % NDB] = E::mfma(a, pf[(i - NSM) / NDB], acc_o[(i - NSM) % NDB]);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                const int nx = i + LEAD;
+                if (nx < NSM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                else if (nx < NM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                // Empty asm statements pin each chain step to its iteration
+                // (pure arithmetic would otherwise float up to the end of the
+                // QK MFMAs); every step depends on its chain's previous pin.
+                const int k = i - NSM - 1;
+                if (k == -1) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        mxc[q] = s[(NEL - 4 + q) / 16][(NEL - 4 + q) % 16];
+                        asm volatile("" : "+v"(mxc[q]));
+                    }
+                }
+                if (k >= 0 && k < NMX) {
+#pragma unroll
+                    for (int e = k * EPS; e < (k + 1) * EPS && e < NEL - 4; ++e)
+                        mxc[k % 4] = fmax_nan(mxc[k % 4], s[e / 16][e % 16]);
+                    asm volatile("" : "+v"(mxc[k % 4]));
+                }
+                if (i >= NSM) __builtin_amdgcn_sched_barrier(0);
+            }
+            m_pre = max_xor32(fmax_nan(fmax_nan(mxc[0], mxc[1]), fmax_nan(mxc[2], mxc[3]))) * scale2;
         } else if (do_pv) {
 #pragma unroll
             for (int i = 0; i < NPVM; ++i)
@@ -304,6 +373,7 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
             for (int i = 0; i < NSM; ++i)
                 s[i % NCB] = E::mfma(qk_operand(kb, i), qf[i / NCB],
                                                                      i < NCB ? zero : s[i % NCB]);
+            if (kMaxInMfma) m_pre = tile_max();
         }
         __builtin_amdgcn_s_setprio(0);
     };
@@ -327,18 +397,12 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
                     if ((r >> 3) * 16 + (r & 7) >= rel) s[c][r] = -INFINITY;
             }
         }
-        // Row max and row sum as several independent chains (a single chain
-        // of dependent max / add instructions would leave the VALU waiting on
-        // its own latency).
+        // Row maximum: from the MFMA step (kMaxInMfma) unless this tile was
+        // just masked.
+        const float m_tile = (!kMaxInMfma || ragged || diag) ? tile_max() : m_pre;
+        // The row sum runs as several independent chains (one chain of
+        // dependent adds would leave the VALU waiting on its own latency).
         constexpr int NCH = 4;
-        float mxc[NCH];
-#pragma unroll
-        for (int k = 0; k < NCH; ++k) mxc[k] = s[0][k];
-#pragma unroll
-        for (int c = 0; c < NCB; ++c)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mxc[r % NCH] = fmax_nan(mxc[r % NCH], s[c][r]);
-        const float m_tile = max_xor32(fmax_nan(fmax_nan(mxc[0], mxc[1]), fmax_nan(mxc[2], mxc[3]))) * scale2;
         // Move the maximum (and rescale O, l) only when some row of the wave
         // outgrew it by more than the threshold.
         if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleThreshold)) {
