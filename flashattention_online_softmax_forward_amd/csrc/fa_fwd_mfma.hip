@@ -182,9 +182,13 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
             const int row = p / CPR;
             qoff[i] = (uint32_t)(row * D + ((p % CPR) ^ (row & (CPR - 1))) * 8) * 2 - (i % 4) * 1024;
         }
-        const int qrows = min(max(Nq - wrow0, 0), 32);
+        // From the wave-uniform index, so the resource is scalar (a per-lane
+        // resource would need a loop over its distinct values).
+        const int qrow0 = q0 + qwave * 32;
+        const int qrows = __builtin_amdgcn_readfirstlane(min(max(Nq - qrow0, 0), 32));
+        const int qfirst = __builtin_amdgcn_readfirstlane(min(qrow0, Nq));
         const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(Q + (size_t)min(wrow0, Nq) * D), (short)0, qrows * D * 2, kBufferRsrcWord3);
+            (void*)(Q + (size_t)qfirst * D), (short)0, qrows * D * 2, kBufferRsrcWord3);
         static_assert(NQS % 4 == 0, "slots in groups of 4");
 #pragma unroll
         for (int g = 0; g < NQS; g += 4)
