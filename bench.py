@@ -258,7 +258,7 @@ def main():
         result["backward"] = {
             "workload": bw.name, "ms_per_call": round(bms, 6), "value": round(btf, 3), "unit": "TFLOP/s",
             "algorithmic_flops": 2.5 * fwd_flops,
-            "roofline": {"kernel": "bwd_rowdot_kernel + bwd_dq_kernel + bwd_dkdv_kernel", "bound": "mfma",
+            "roofline": {"kernel": "bwd_dq_kernel + bwd_dkdv_kernel", "bound": "mfma",
                          "achieved": round(btf, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(btf / PEAK_BF16_TFLOPS, 4),
                          "traffic": measured_traffic(f"bwd_kernels_{bw.name}", bdigest),

@@ -2,7 +2,7 @@
 // and section 11.9 of the ML compiler page: only O and the per-row
 // log-sum-exp L are kept from the forward pass; P is recomputed block by block
 // as exp(S - L)). For one (batch, head):
-//     D_i = sum_d dO[i,d] O[i,d]                       (bwd_rowdot_kernel)
+//     D_i = sum_d dO[i,d] O[i,d]                       (bwd_dq_kernel, stored)
 //     P = exp(scale Q K^T - L),  dP = dO V^T,  dS = P * (dP - D)
 //     dQ = scale dS K                                  (bwd_dq_kernel)
 //     dV = P^T dO,  dK = scale dS^T Q                  (bwd_dkdv_kernel)
@@ -233,35 +233,13 @@ __device__ __forceinline__ void mfma_stream(Op op, Step step) {
 
 }  // namespace
 
-// D_i = sum_d dO[i,d] O[i,d] in fp32: D/8 lanes per row, 8 elements each.
-template <typename T, int D>
-__global__ __launch_bounds__(256)
-void bwd_rowdot_kernel(const uint16_t* __restrict__ Og, const uint16_t* __restrict__ dOg,
-                       float* __restrict__ Dg, long long rows) {
-    constexpr int LPR = D / 8;
-    constexpr int RPB = 256 / LPR;
-    const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
-    const int sub = threadIdx.x % LPR;
-    float acc = 0.f;
-    if (row < rows) {
-        const u32x4_t a = *(const u32x4_t*)(Og + row * D + sub * 8);
-        const u32x4_t b = *(const u32x4_t*)(dOg + row * D + sub * 8);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc = __builtin_fmaf(Elem<T>::lo(a[i]), Elem<T>::lo(b[i]), acc);
-            acc = __builtin_fmaf(Elem<T>::hi(a[i]), Elem<T>::hi(b[i]), acc);
-        }
-    }
-    acc = group_sum<LPR>(acc);
-    if (row < rows && sub == 0) Dg[row] = acc;
-}
-
-// dQ for 128 query rows of one (batch, head), streaming K and V tiles.
+// dQ for 128 query rows of one (batch, head), streaming K and V tiles; also
+// D of those rows, which the dK/dV kernel reads.
 template <typename T, int D>
 __global__ __launch_bounds__(kBwdThreads, 2)
 void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
-                   const uint16_t* __restrict__ Vg, const uint16_t* __restrict__ dOg,
-                   const float* __restrict__ LSEg, const float* __restrict__ Dg,
+                   const uint16_t* __restrict__ Vg, const uint16_t* __restrict__ Og,
+                   const uint16_t* __restrict__ dOg, const float* __restrict__ LSEg, float* __restrict__ Dg,
                    uint16_t* __restrict__ dQg, const int* __restrict__ kv_lens, int H, int Nq, int Nk,
                    int nqb, float scale, float scale2, int causal) {
     using V8 = typename Elem<T>::v8;
@@ -298,7 +276,26 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
     load_b_rows<T, D>(Qg + (size_t)bh * Nq * D, qrow, qvalid, h, qf);
     load_b_rows<T, D>(dOg + (size_t)bh * Nq * D, qrow, qvalid, h, dof);
     const float l2 = qvalid ? LSEg[(size_t)bh * Nq + qrow] * kLog2e : 0.f;
-    const float dr = qvalid ? Dg[(size_t)bh * Nq + qrow] : 0.f;
+    // D of this row, sum_d dO O in fp32 from the same B-operand layout (lane
+    // (j, h) holds half of row j), written for the dK/dV kernel.
+    float dr;
+    {
+        V8 of[NKK];
+        load_b_rows<T, D>(Og + (size_t)bh * Nq * D, qrow, qvalid, h, of);
+        float acc[2] = {0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            const u32x4_t a = __builtin_bit_cast(u32x4_t, of[kk]);
+            const u32x4_t b = __builtin_bit_cast(u32x4_t, dof[kk]);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                acc[w & 1] = __builtin_fmaf(Elem<T>::lo(a[w]), Elem<T>::lo(b[w]), acc[w & 1]);
+                acc[w & 1] = __builtin_fmaf(Elem<T>::hi(a[w]), Elem<T>::hi(b[w]), acc[w & 1]);
+            }
+        }
+        dr = sum_xor32(acc[0] + acc[1]);
+        if (qvalid && h == 0) Dg[(size_t)bh * Nq + qrow] = dr;
+    }
 
     TileOffsets<D> off;
     off.init(lane);
@@ -601,18 +598,12 @@ template <typename T, int D>
 static hipError_t launch_bwd_d(const BwdArgs& a) {
     const float scale2 = a.scale * kLog2e;
     if (a.Nq > 0) {
-        const long long rows = (long long)a.B * a.H * a.Nq;
-        constexpr int RPB = 256 / (D / 8);
-        hipLaunchKernelGGL((bwd_rowdot_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
-                           a.stream, (const uint16_t*)a.O, (const uint16_t*)a.dO, a.Dvec, rows);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
         const int nqb = (a.Nq + BM_BWD - 1) / BM_BWD;
         hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3(a.B * a.H * nqb), dim3(kBwdThreads), 0, a.stream,
                            (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
-                           (const uint16_t*)a.dO, a.LSE, a.Dvec, (uint16_t*)a.dQ, a.kv_lens, a.H, a.Nq, a.Nk,
-                           nqb, a.scale, scale2, a.causal);
-        e = hipGetLastError();
+                           (const uint16_t*)a.O, (const uint16_t*)a.dO, a.LSE, a.Dvec, (uint16_t*)a.dQ,
+                           a.kv_lens, a.H, a.Nq, a.Nk, nqb, a.scale, scale2, a.causal);
+        hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     // With Nq = 0 the dK/dV kernel stages only V, runs no query tile and
