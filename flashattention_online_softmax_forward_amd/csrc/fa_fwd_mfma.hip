@@ -17,7 +17,8 @@
 // gfx950 mapping (own design):
 //   * 8 waves x 32 query rows, one workgroup per CU (2 waves per SIMD). Q stays
 //     in VGPRs for the whole key loop as the B operand of
-//     v_mfma_f32_32x32x16_bf16.
+//     v_mfma_f32_32x32x16_bf16. Q arrives, and O leaves, through an LDS row
+//     staging area, so that both move whole rows between HBM and the CU.
 //   * S is computed transposed, S^T = K Q^T (A = 32 keys of K from LDS), so that
 //     every lane ends with 16 scores of ONE query row: the row max / row sum are
 //     in-lane reductions plus one exchange with lane ^ 32.
@@ -27,8 +28,8 @@
 //     registers.
 //   * O^T lives in 16*D/32 fp32 accumulators per lane, one query row per lane,
 //     so the alpha rescale is a per-lane scalar multiply.
-//   * Ping-pong: every wave alternates an MFMA step (PV of the previous tile,
-//     then QK of the current one) and a softmax step, separated by workgroup
+//   * Ping-pong: every wave alternates an MFMA step (PV of the previous tile
+//     and QK of the current one) and a softmax step, separated by workgroup
 //     barriers; the two wave groups (waves 0-3 and 4-7, one of each per SIMD)
 //     run a step apart, so on every SIMD one wave feeds the matrix core while
 //     the other runs the exponentials on the VALU.
