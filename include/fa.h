@@ -263,8 +263,8 @@ size_t fa_backward_workspace_bytes(int B, int H, int Nq);
  *   looked at. Nk == 0 < Nq: FA_ERR_INVALID_ARG (the forward pass is
  *   undefined there).
  * Products use bf16 MFMA with fp32 accumulation; P and dS are rounded to bf16
- * before the products that consume them. Three kernels run on `stream`: the
- * row dot products D, then dQ, then dK and dV.
+ * before the products that consume them. Two kernels run on `stream`: dQ
+ * (which also forms D and stores it in the workspace), then dK and dV.
  */
 fa_status fa_backward(const void* Q, const void* K, const void* V,
                       const void* O, const void* dO, const float* LSE,
