@@ -416,8 +416,11 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     const int k0 = kb * BM_BWD;
     const int kw0 = k0 + wave * 32;
     const int krow = kw0 + j;
-    const bool kvalid = krow < Nk;
     const int Lk = real_keys(kv_lens, bh / H, Nk);
+    // Keys past Lk (padding) are never read: their K rows and V rows are
+    // zeros here, so S = dP = 0 and, with P = 0, dS = 0 exactly whatever the
+    // padded cache holds (a NaN there would otherwise survive 0 * NaN).
+    const bool kvalid = krow < Lk;
     const int doff = causal == kCausalBottomRight ? Lk - Nq : 0;   // key j visible from query i iff j <= i + doff
 
     const uint16_t* Q = Qg + (size_t)bh * Nq * D;
@@ -552,11 +555,11 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
                                    });
     };
 
-    // Prologue: the block's V rows (zeros past Nk) and the first tile.
+    // Prologue: the block's V rows (zeros past Lk) and the first tile.
     {
         StageSlots<D, BM_BWD> vslots;
         vslots.init(wave, lane);
-        vslots.stage(Vg + ((size_t)bh * Nk + k0) * D, min(Nk - k0, BM_BWD), v_blk, wave);
+        vslots.stage(Vg + ((size_t)bh * Nk + k0) * D, max(0, min(Lk - k0, BM_BWD)), v_blk, wave);
     }
     if (first < nqt) {
         stage(first, q_lds0, o_lds0);

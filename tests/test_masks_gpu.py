@@ -129,6 +129,46 @@ def test_padding_ignores_padded_values(fa):
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
+def _garbage_padding(k, v, lens):
+    """K/V copies whose padded keys hold NaN, +inf and huge values."""
+    k2, v2 = k.clone(), v.clone()
+    for b, L in enumerate(lens):
+        k2[b, :, L:] = float("nan")
+        v2[b, :, L::2] = float("inf")
+        v2[b, :, L + 1::2] = float("nan")
+    return k2, v2
+
+
+def test_padding_ignores_nan_keys_forward_backward_decode(fa):
+    """Padded keys holding NaN or inf leave every output bitwise unchanged:
+    forward (both causal alignments), backward (dK, dV of padded keys are 0)
+    and split-KV decode. Lengths end inside a tile, on a tile edge and at 0."""
+    lens_list = [150, 64, 0]
+    lens = lens_tensor(lens_list)
+    q, k, v = synth.make_qkv(3, 2, 100, 200, 128, torch.bfloat16, seed=45, device=DEV)
+    k2, v2 = _garbage_padding(k, v, lens_list)
+    do = synth.make_do(3, 2, 100, 128, torch.bfloat16, seed=45).to(DEV)
+    for causal in (0, 2):
+        o_a, l_a = fa.fa_forward(q, k, v, causal=causal, kv_lens=lens)
+        o_b, l_b = fa.fa_forward(q, k2, v2, causal=causal, kv_lens=lens)
+        ga = fa.fa_backward(q, k, v, o_a, do, l_a, causal=causal, kv_lens=lens)
+        gb = fa.fa_backward(q, k2, v2, o_b, do, l_b, causal=causal, kv_lens=lens)
+        torch.cuda.synchronize()
+        assert torch.equal(o_a, o_b) and torch.equal(l_a, l_b), f"forward causal={causal}"
+        for name, x, y in zip(("dq", "dk", "dv"), ga, gb):
+            assert torch.equal(x, y), f"backward {name} causal={causal}"
+        for b, L in enumerate(lens_list):
+            assert not gb[1][b, :, L:].any() and not gb[2][b, :, L:].any(), f"padded dK/dV b={b}"
+    qd, kd, vd = synth.make_qkv(3, 2, 1, 333, 64, torch.bfloat16, seed=46, device=DEV)
+    dlens = [333, 65, 0]
+    kd2, vd2 = _garbage_padding(kd, vd, dlens)
+    la = lens_tensor(dlens)
+    oa, sa = fa.fa_decode_splitkv(qd, kd, vd, 8, kv_lens=la)
+    ob, sb = fa.fa_decode_splitkv(qd, kd2, vd2, 8, kv_lens=la)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ob) and torch.equal(sa, sb)
+
+
 DEC_CASES = [
     # (B, H, Nk, D, splits, kv_lens)
     (4, 8, 5000, 128, 16, [5000, 1, 0, 2049]),
