@@ -365,6 +365,12 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
     // Tile t in buffer t % 2; the next tile is loaded while t is computed and
     // published by the barrier that ends the iteration.
     for (int t = 0; t < ntiles; t += 2) {
+        // Two workgroups share a CU. Left alone, one of them takes most of
+        // the issue slots (measured per workgroup: two clusters of key-loop
+        // times, ~72 and ~85 us, at 2048 keys); priorities that alternate by
+        // tile pair and block parity even them out (one cluster, ~83 us).
+        if (((t >> 1) + blockIdx.x) & 1) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
         if (t + 1 < ntiles) stage(t + 1, k_lds1, v_lds1);
         if (t < my_tiles) compute(t, k_lds0, v_lds0);
         lds_dma_wait_all();
@@ -570,6 +576,9 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     __syncthreads();
     // Tile first + 2i in buffer 0, first + 2i + 1 in buffer 1.
     for (int u = first; u < nqt; u += 2) {
+        // Alternating priorities, as in the dQ kernel (two workgroups per CU).
+        if ((((u - first) >> 1) + blockIdx.x) & 1) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
         if (u + 1 < nqt) {
             stage(u + 1, q_lds1, o_lds1);
             fetch_ld(u + 1);
