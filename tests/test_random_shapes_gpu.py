@@ -76,7 +76,7 @@ def check(tag, o, lse, ro, rl, dtype, mul=1.0):
             f"{tag}: O max {err_o.max():.3e} mean {err_o.mean():.3e} LSE {err_l.max():.3e}"
 
 
-SEEDS = list(range(1000, 1024))
+SEEDS = list(range(1000, 1048))
 
 
 @pytest.mark.parametrize("seed", SEEDS)
@@ -118,7 +118,7 @@ def test_random_forward_and_backward(fa, seed):
                         f"seed {seed} {dtype} {name} ({b},{h}) err/bound {ratio.max():.3f} {case}"
 
 
-@pytest.mark.parametrize("seed", list(range(2000, 2008)))
+@pytest.mark.parametrize("seed", list(range(2000, 2016)))
 def test_random_decode(fa, seed):
     r = np.random.default_rng(seed)
     B, H = int(r.integers(1, 5)), int(r.integers(1, 5))
