@@ -116,19 +116,26 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 // no swizzle, no index stride.
 constexpr int kBufferRsrcWord3 = 0x00020000;
 
+// Cache-policy bits of a buffer access on gfx9.4-family parts (gfx950
+// included): NT marks the line non-temporal, so L2 streams it instead of
+// keeping it for reuse. Used for data one workgroup touches once, which would
+// otherwise push out K/V lines that other workgroups of the head re-read.
+constexpr int kCachePolicyNT = 2;
+
 // Slots I .. N-1 (N <= 4) of a wave's share of a tile load into LDS
 // (buffer_load_dwordx4 with the lds bit): slot I moves 16 bytes per lane from
 // the resource at voff[I] + 1 KB * I to base + 1 KB * I + 16 * lane. The
 // immediate offset supplies the 1 KB step (it moves the LDS destination and
 // the memory address alike), so voff[I] is stored net of it. A lane whose
-// offset is past the resource's size writes zeros.
-template <int N, int I = 0>
+// offset is past the resource's size writes zeros. POLICY holds the cache
+// policy bits (0 or kCachePolicyNT).
+template <int N, int I = 0, int POLICY = 0>
 __device__ __forceinline__ void buffer_lds_slots(__amdgpu_buffer_rsrc_t rsrc, __attribute__((address_space(3))) void* base,
                                                  const uint32_t* voff) {
     static_assert(N <= 4, "the immediate offset field holds at most 3 KB");
     if constexpr (I < N) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, base, 16, voff[I], 0, I * 1024, 0);
-        buffer_lds_slots<N, I + 1>(rsrc, base, voff);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, base, 16, voff[I], 0, I * 1024, POLICY);
+        buffer_lds_slots<N, I + 1, POLICY>(rsrc, base, voff);
     }
 }
 

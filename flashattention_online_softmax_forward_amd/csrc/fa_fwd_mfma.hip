@@ -191,9 +191,10 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
         const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(Q + (size_t)qfirst * D), (short)0, qrows * D * 2, kBufferRsrcWord3);
         static_assert(NQS % 4 == 0, "slots in groups of 4");
+        // Each Q row is read by one workgroup only: streamed past L2.
 #pragma unroll
         for (int g = 0; g < NQS; g += 4)
-            buffer_lds_slots<4>(rsrc, (LDS_AS void*)(LDS_AS uint16_t*)(qst + g * 512), qoff + g);
+            buffer_lds_slots<4, 0, kCachePolicyNT>(rsrc, (LDS_AS void*)(LDS_AS uint16_t*)(qst + g * 512), qoff + g);
     }
     // Q as the B operand: lane (j, h) holds row qrow, d = 16*kk + 8*h .. +7.
     u32x4_t qw[NKK];
@@ -558,7 +559,9 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     const float l_tot = sum_xor32(l_run);
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     // O goes out through the wave's row staging (its Q reads ended before
-    // the key loop) so that every store writes whole rows.
+    // the key loop) so that every store writes whole rows. O and LSE are
+    // stored non-temporal: nothing here reads them again, and they would
+    // otherwise take L2 lines that hold other workgroups' K/V tiles.
     {
         uint16_t* ost = qst;
 #pragma unroll
@@ -587,10 +590,10 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
         uint16_t* orow = Og + ((size_t)bh * Nq + wrow0 + lane / CPR) * D + c * 8;
 #pragma unroll
         for (int it = 0; it < NIT; ++it)
-            if (wrow0 + it * RPI + lane / CPR < Nq) *(u32x4_t*)(orow + it * RPI * D) = w[it];
+            if (wrow0 + it * RPI + lane / CPR < Nq) __builtin_nontemporal_store(w[it], (u32x4_t*)(orow + it * RPI * D));
     }
     if (qrow < Nq && h == 0 && LSEg)
-        LSEg[(size_t)bh * Nq + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+        __builtin_nontemporal_store(l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY, &LSEg[(size_t)bh * Nq + qrow]);
 }
 
 template <typename T, int D>
