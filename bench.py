@@ -43,11 +43,19 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "flashattention_online_softmax_forward_amd", "csrc")
 
 
+def _code_only(text):
+    """Source text without comments, trailing blanks or empty lines, so that a
+    comment edit leaves the digest of a kernel's code unchanged."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", line).rstrip() for line in text.splitlines())
+    return "\n".join(line for line in lines if line)
+
+
 def kernel_source_digest(files):
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -116,9 +116,9 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 // no swizzle, no index stride.
 constexpr int kBufferRsrcWord3 = 0x00020000;
 
-// Cache-policy bits of a buffer access on gfx9.4-family parts (gfx950
-// included): NT marks the line non-temporal, so L2 streams it instead of
-// keeping it for reuse. Used for data one workgroup touches once, which would
+// Cache-policy operand of a buffer access on gfx950 (the gfx940 encoding:
+// bit 0 SC0, bit 1 NT, bit 4 SC1). NT marks the line non-temporal, so L2
+// streams it instead of keeping it for reuse. Used for data one workgroup touches once, which would
 // otherwise push out K/V lines that other workgroups of the head re-read.
 constexpr int kCachePolicyNT = 2;
 
