@@ -18,7 +18,9 @@
 //   * 8 waves x 32 query rows, one workgroup per CU (2 waves per SIMD). Q stays
 //     in VGPRs for the whole key loop as the B operand of
 //     v_mfma_f32_32x32x16_bf16. Q arrives, and O leaves, through an LDS row
-//     staging area, so that both move whole rows between HBM and the CU.
+//     staging area, so that both move whole rows between HBM and the CU. Both
+//     carry the non-temporal cache policy (each is touched once), which leaves
+//     L2 to the K/V tiles that every query block of a head re-reads.
 //   * S is computed transposed, S^T = K Q^T (A = 32 keys of K from LDS), so that
 //     every lane ends with 16 scores of ONE query row: the row max / row sum are
 //     in-lane reductions plus one exchange with lane ^ 32.
