@@ -57,17 +57,39 @@ def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def _check_tensor(name: str, t: torch.Tensor, dtype: torch.dtype, ndim: int = 4) -> None:
+def _check_layout(name: str, t, dtype: torch.dtype, shape=None, ndim: int = 4) -> None:
+    """Type, dtype, rank, exact shape (when given) and contiguity; device-free,
+    so a wrong-shaped tensor is refused before anything else is looked at."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name} must live on a ROCm GPU (got {t.device}); there is no CPU path")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
-    if t.dim() != ndim:
+    if shape is not None:
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    elif t.dim() != ndim:
         raise ValueError(f"{name} must be {ndim}-D [B, H, N, D] (got shape {tuple(t.shape)})")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _check_devices(ref: torch.Tensor, **tensors) -> None:
+    """Every tensor on the one ROCm device of ``ref``; None entries are skipped."""
+    if ref.device.type != "cuda":
+        raise ValueError(f"tensors must live on a ROCm GPU (got {ref.device}); there is no CPU path")
+    for name, t in tensors.items():
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} must live on {ref.device} (got {t.device})")
+
+
+def _check_workspace(workspace, need: int) -> int:
+    """A contiguous tensor of at least ``need`` bytes; returns its size in bytes."""
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous torch.Tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    if nbytes < need:
+        raise ValueError(f"workspace holds {nbytes} bytes; {need} are needed")
+    return nbytes
 
 
 def _causal_mode(causal) -> int:
@@ -82,39 +104,41 @@ def _causal_mode(causal) -> int:
     return mode
 
 
-def _check_kv_lens(kv_lens, B, device):
+def _check_kv_lens(kv_lens, B):
     if kv_lens is None:
         return None
     if not isinstance(kv_lens, torch.Tensor) or kv_lens.dtype != torch.int32 or kv_lens.dim() != 1 \
             or kv_lens.shape[0] != B or not kv_lens.is_contiguous():
         raise ValueError(f"kv_lens must be a contiguous int32 tensor of shape [{B}]")
-    if kv_lens.device != device:
-        raise ValueError(f"kv_lens must live on {device} (got {kv_lens.device})")
     return kv_lens
 
 
-def _forward(fn_name, dtype, q, k, v, causal, scale, out, lse, want_lse, kv_lens=None):
+def _check_qkv(q, k, v, dtype):
+    """q [B,H,Nq,D], k and v [B,H,Nk,D] of one dtype; returns (B, H, Nq, Nk, D)."""
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_tensor(name, t, dtype)
+        _check_layout(name, t, dtype)
     B, H, Nq, D = q.shape
     Nk = k.shape[2]
     if tuple(k.shape) != (B, H, Nk, D) or tuple(v.shape) != (B, H, Nk, D):
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    return B, H, Nq, Nk, D
+
+
+def _forward(fn_name, dtype, q, k, v, causal, scale, out, lse, want_lse, kv_lens=None):
+    B, H, Nq, Nk, D = _check_qkv(q, k, v, dtype)
+    if out is not None:
+        _check_layout("out", out, dtype, q.shape)
+    if lse is not None:
+        _check_layout("lse", lse, torch.float32, (B, H, Nq))
+    kv_lens = _check_kv_lens(kv_lens, B)
+    mode = _causal_mode(causal)
+    _check_devices(q, k=k, v=v, out=out, lse=lse, kv_lens=kv_lens)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
-    _check_tensor("out", out, dtype)
-    if tuple(out.shape) != tuple(q.shape):
-        raise ValueError("out must have q's shape")
     if lse is None and want_lse:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        _check_tensor("lse", lse, torch.float32, ndim=3)
-        if tuple(lse.shape) != (B, H, Nq):
-            raise ValueError("lse must be [B, H, Nq]")
-    mode = _causal_mode(causal)
-    kv_lens = _check_kv_lens(kv_lens, B, q.device)
     lib = _lib.load()
     lse_p = lse.data_ptr() if lse is not None else None
     if kv_lens is None:
@@ -159,6 +183,21 @@ def fa_decode_workspace_bytes(B: int, H: int, D: int, num_splits: int) -> int:
     return int(_lib.load().fa_decode_workspace_bytes(B, H, D, num_splits))
 
 
+def _check_decode(q, k, v, out, lse, kv_lens):
+    """Shapes of a decode call (device-free); returns (B, H, Nk, D)."""
+    if not isinstance(q, torch.Tensor) or q.dtype not in _DTYPES:
+        raise TypeError(f"q must be a bfloat16 or float16 tensor (got {getattr(q, 'dtype', type(q))})")
+    B, H, one, Nk, D = _check_qkv(q, k, v, q.dtype)
+    if one != 1:
+        raise ValueError("decode takes exactly one query token per (batch, head)")
+    if out is not None:
+        _check_layout("out", out, q.dtype, q.shape)
+    if lse is not None:
+        _check_layout("lse", lse, torch.float32, (B, H))
+    _check_kv_lens(kv_lens, B)
+    return B, H, Nk, D
+
+
 def fa_decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, num_splits: int,
                       scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
@@ -170,32 +209,19 @@ def fa_decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, num_spl
     ``workspace`` is a device tensor of at least
     fa_decode_workspace_bytes(B,H,D,num_splits) bytes; one is allocated when
     not given."""
-    if q.dtype not in _DTYPES:
-        raise TypeError(f"q must be bfloat16 or float16 (got {q.dtype})")
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_tensor(name, t, q.dtype)
-    B, H, one, D = q.shape
-    Nk = k.shape[2]
-    if one != 1:
-        raise ValueError("decode takes exactly one query token per (batch, head)")
-    if tuple(k.shape) != (B, H, Nk, D) or tuple(v.shape) != (B, H, Nk, D):
-        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    B, H, Nk, D = _check_decode(q, k, v, out, lse, kv_lens)
+    need = fa_decode_workspace_bytes(B, H, D, num_splits)
+    ws_bytes = _check_workspace(workspace, need) if workspace is not None else None
+    _check_devices(q, k=k, v=v, out=out, lse=lse, kv_lens=kv_lens, workspace=workspace)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    need = fa_decode_workspace_bytes(B, H, D, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    if workspace.device != q.device or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous tensor on q's device")
-    ws_bytes = workspace.numel() * workspace.element_size()
+        ws_bytes = workspace.numel()
     if out is None:
         out = torch.empty_like(q)
-    _check_tensor("out", out, q.dtype)
     if lse is None and want_lse:
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        _check_tensor("lse", lse, torch.float32, ndim=2)
-    kv_lens = _check_kv_lens(kv_lens, B, q.device)
     lse_p = lse.data_ptr() if lse is not None else None
     lib = _lib.load()
     name = "fa_decode_splitkv" + ("_f16" if q.dtype == torch.float16 else "")
@@ -227,36 +253,28 @@ def fa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tens
     kv_lens). Returns (dQ, dK, dV) in the input type with the shapes of q, k,
     v. ``workspace`` holds at least fa_backward_workspace_bytes(B,H,Nq) bytes;
     one is allocated when not given."""
-    if q.dtype not in _DTYPES:
-        raise TypeError(f"q must be bfloat16 or float16 (got {q.dtype})")
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
-        _check_tensor(name, t, q.dtype)
-    B, H, Nq, D = q.shape
-    Nk = k.shape[2]
-    if tuple(k.shape) != (B, H, Nk, D) or tuple(v.shape) != (B, H, Nk, D):
-        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
-    if tuple(o.shape) != tuple(q.shape) or tuple(do.shape) != tuple(q.shape):
-        raise ValueError("o and do must have q's shape")
-    _check_tensor("lse", lse, torch.float32, ndim=3)
-    if tuple(lse.shape) != (B, H, Nq):
-        raise ValueError("lse must be [B, H, Nq]")
+    if not isinstance(q, torch.Tensor) or q.dtype not in _DTYPES:
+        raise TypeError(f"q must be a bfloat16 or float16 tensor (got {getattr(q, 'dtype', type(q))})")
+    B, H, Nq, Nk, D = _check_qkv(q, k, v, q.dtype)
+    _check_layout("o", o, q.dtype, q.shape)
+    _check_layout("do", do, q.dtype, q.shape)
+    _check_layout("lse", lse, torch.float32, (B, H, Nq))
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t is not None:
+            _check_layout(name, t, q.dtype, ref.shape)
+    _check_kv_lens(kv_lens, B)
+    mode = _causal_mode(causal)
+    need = fa_backward_workspace_bytes(B, H, Nq)
+    ws_bytes = _check_workspace(workspace, need) if workspace is not None else None
+    _check_devices(q, k=k, v=v, o=o, do=do, lse=lse, dq=dq, dk=dk, dv=dv, kv_lens=kv_lens, workspace=workspace)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    need = fa_backward_workspace_bytes(B, H, Nq)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    if workspace.device != q.device or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous tensor on q's device")
-    ws_bytes = workspace.numel() * workspace.element_size()
+        ws_bytes = workspace.numel()
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
-        _check_tensor(name, t, q.dtype)
-        if tuple(t.shape) != tuple(ref.shape):
-            raise ValueError(f"{name} must have the shape {tuple(ref.shape)}")
-    mode = _causal_mode(causal)
-    kv_lens = _check_kv_lens(kv_lens, B, q.device)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr())
     outs = (dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), ws_bytes)
     lib = _lib.load()
@@ -282,13 +300,12 @@ def _rope_style(style) -> int:
     return int(style)
 
 
-def _check_tables(cos, sin, D, device):
+def _check_tables(cos, sin, D):
+    """cos, sin fp32 [n_pos, D/2] of one shape (device-free); returns n_pos."""
     for name, t in (("cos", cos), ("sin", sin)):
-        _check_tensor(name, t, torch.float32, ndim=2)
+        _check_layout(name, t, torch.float32, ndim=2)
         if t.shape[1] != D // 2:
             raise ValueError(f"{name} must be [n_pos, {D // 2}]")
-        if t.device != device:
-            raise ValueError(f"{name} must live on {device}")
     if cos.shape != sin.shape:
         raise ValueError("cos and sin must have the same shape")
     return cos.shape[0]
@@ -298,17 +315,18 @@ def fa_rope(x: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor, style="half",
             out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Rotary position embedding of x [B,H,N,D] (bf16 or fp16): row n rotated by
     cos[n], sin[n] (fp32 [n_pos, D/2]). ``out`` may be ``x`` (in place)."""
-    if x.dtype not in _DTYPES:
-        raise TypeError(f"x must be bfloat16 or float16 (got {x.dtype})")
-    _check_tensor("x", x, x.dtype)
+    if not isinstance(x, torch.Tensor) or x.dtype not in _DTYPES:
+        raise TypeError(f"x must be a bfloat16 or float16 tensor (got {getattr(x, 'dtype', type(x))})")
+    _check_layout("x", x, x.dtype)
     B, H, N, D = x.shape
-    n_pos = _check_tables(cos, sin, D, x.device)
+    n_pos = _check_tables(cos, sin, D)
+    if out is not None:
+        _check_layout("out", out, x.dtype, x.shape)
+    st = _rope_style(style)
+    _check_devices(x, cos=cos, sin=sin, out=out)
     out = torch.empty_like(x) if out is None else out
-    _check_tensor("out", out, x.dtype)
-    if out.shape != x.shape:
-        raise ValueError("out must have x's shape")
     code = _lib.load().fa_rope(x.data_ptr(), out.data_ptr(), cos.data_ptr(), sin.data_ptr(), n_pos,
-                               _rope_style(style), _DTYPES[x.dtype], B, H, N, D, _stream(x))
+                               st, _DTYPES[x.dtype], B, H, N, D, _stream(x))
     _lib.check(code, "fa_rope")
     return out
 
@@ -326,31 +344,31 @@ def fa_forward_rope(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cos: torc
     """Forward pass of rope(Q), rope(K), V (bf16 or fp16): key j at position j,
     query i at position i (i + Lk - Nq under bottom-right alignment).
     Returns (O [B,H,Nq,D] in the input type, LSE fp32 [B,H,Nq] or None)."""
-    if q.dtype not in _DTYPES:
-        raise TypeError(f"q must be bfloat16 or float16 (got {q.dtype})")
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_tensor(name, t, q.dtype)
-    B, H, Nq, D = q.shape
-    Nk = k.shape[2]
-    if tuple(k.shape) != (B, H, Nk, D) or tuple(v.shape) != (B, H, Nk, D):
-        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
-    n_pos = _check_tables(cos, sin, D, q.device)
+    if not isinstance(q, torch.Tensor) or q.dtype not in _DTYPES:
+        raise TypeError(f"q must be a bfloat16 or float16 tensor (got {getattr(q, 'dtype', type(q))})")
+    B, H, Nq, Nk, D = _check_qkv(q, k, v, q.dtype)
+    n_pos = _check_tables(cos, sin, D)
+    if out is not None:
+        _check_layout("out", out, q.dtype, q.shape)
+    if lse is not None:
+        _check_layout("lse", lse, torch.float32, (B, H, Nq))
+    _check_kv_lens(kv_lens, B)
+    st, mode = _rope_style(style), _causal_mode(causal)
+    need = fa_rope_workspace_bytes(B, H, Nk, D)
+    ws_bytes = _check_workspace(workspace, need) if workspace is not None else None
+    _check_devices(q, k=k, v=v, cos=cos, sin=sin, out=out, lse=lse, kv_lens=kv_lens, workspace=workspace)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     out = torch.empty_like(q) if out is None else out
-    _check_tensor("out", out, q.dtype)
     if lse is None and want_lse:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        _check_tensor("lse", lse, torch.float32, ndim=3)
-    need = fa_rope_workspace_bytes(B, H, Nk, D)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    kv_lens = _check_kv_lens(kv_lens, B, q.device)
+        ws_bytes = workspace.numel()
     code = _lib.load().fa_forward_rope(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr() if lse is not None else None,
         kv_lens.data_ptr() if kv_lens is not None else None, cos.data_ptr(), sin.data_ptr(), n_pos,
-        _rope_style(style), _DTYPES[q.dtype], workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-        B, H, Nq, Nk, D, float(scale), _causal_mode(causal), _stream(q))
+        st, _DTYPES[q.dtype], workspace.data_ptr(), ws_bytes,
+        B, H, Nq, Nk, D, float(scale), mode, _stream(q))
     _lib.check(code, "fa_forward_rope")
     return out, lse

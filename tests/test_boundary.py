@@ -248,3 +248,58 @@ def test_product_path_does_not_import_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), f"{f} mentions the oracle"
+
+
+def test_python_binding_checks_caller_buffers_before_the_device(lib):
+    """A caller-supplied out / lse / workspace of the wrong shape or size is
+    refused by its shape before the device is looked at, so on the CPU the
+    shape error is the one raised, and no call reaches the library."""
+    import torch
+
+    import flashattention_online_softmax_forward_amd as fa
+
+    bf = torch.bfloat16
+    q = torch.zeros(2, 3, 8, 64, dtype=bf)
+    kv = torch.zeros(2, 3, 16, 64, dtype=bf)
+    lse = torch.zeros(2, 3, 8)
+    with pytest.raises(ValueError, match="out must have shape"):
+        fa.fa_forward(q, kv, kv, out=torch.zeros(2, 3, 7, 64, dtype=bf))
+    with pytest.raises(ValueError, match="lse must have shape"):
+        fa.fa_forward(q, kv, kv, lse=torch.zeros(2, 3, 4))
+
+    q1 = torch.zeros(2, 3, 1, 64, dtype=bf)
+    with pytest.raises(ValueError, match="out must have shape"):
+        fa.fa_decode_splitkv(q1, kv, kv, num_splits=4, out=torch.zeros(1, 3, 1, 64, dtype=bf))
+    with pytest.raises(ValueError, match="lse must have shape"):
+        fa.fa_decode_splitkv(q1, kv, kv, num_splits=4, lse=torch.zeros(2, 2))
+    with pytest.raises(ValueError, match="lse must have shape"):
+        fa.fa_decode_splitkv(q1, kv, kv, num_splits=4, lse=torch.zeros(2, 3, 1))
+    need = fa.fa_decode_workspace_bytes(2, 3, 64, 4)
+    with pytest.raises(ValueError, match="workspace holds"):
+        fa.fa_decode_splitkv(q1, kv, kv, num_splits=4, workspace=torch.zeros(need - 1, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="contiguous"):
+        fa.fa_decode_splitkv(q1, kv, kv, num_splits=4, workspace=torch.zeros(2 * need, dtype=torch.uint8)[::2])
+
+    cos = torch.zeros(16, 32)
+    with pytest.raises(ValueError, match="out must have shape"):
+        fa.fa_forward_rope(q, kv, kv, cos, cos, out=torch.zeros(2, 3, 8, 128, dtype=bf))
+    with pytest.raises(ValueError, match="lse must have shape"):
+        fa.fa_forward_rope(q, kv, kv, cos, cos, lse=torch.zeros(2, 3, 16))
+    need = fa.fa_rope_workspace_bytes(2, 3, 16, 64)
+    with pytest.raises(ValueError, match="workspace holds"):
+        fa.fa_forward_rope(q, kv, kv, cos, cos, workspace=torch.zeros(need // 2, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="contiguous"):
+        fa.fa_forward_rope(q, kv, kv, cos, cos, workspace=torch.zeros(2 * need, dtype=torch.uint8)[::2])
+
+    with pytest.raises(ValueError, match="dk must have shape"):
+        fa.fa_backward(q, kv, kv, q, q, lse, dk=torch.zeros(2, 3, 8, 64, dtype=bf))
+    with pytest.raises(ValueError, match="lse must have shape"):
+        fa.fa_backward(q, kv, kv, q, q, torch.zeros(2, 3, 16))
+    with pytest.raises(ValueError, match="workspace holds"):
+        fa.fa_backward(q, kv, kv, q, q, lse, workspace=torch.zeros(4, dtype=torch.uint8))
+
+    # Right shapes everywhere: the device check is what refuses them.
+    with pytest.raises(ValueError, match="ROCm GPU"):
+        fa.fa_decode_splitkv(q1, kv, kv, num_splits=4, out=torch.zeros_like(q1), lse=torch.zeros(2, 3))
+    with pytest.raises(ValueError, match="ROCm GPU"):
+        fa.fa_forward_rope(q, kv, kv, cos, cos, out=torch.zeros_like(q), lse=lse)
