@@ -25,6 +25,7 @@ from . import _lib
 CAUSAL_NONE, CAUSAL_TOP_LEFT, CAUSAL_BOTTOM_RIGHT = 0, 1, 2
 ROPE_HALF, ROPE_PAIRS = 0, 1
 _DTYPES = {torch.bfloat16: 0, torch.float16: 1}
+DECODE_NOALLOC_SCRATCH_BYTES = 32 << 20   # FA_DECODE_NOALLOC_SCRATCH_BYTES of include/fa.h
 
 __all__ = [
     "CAUSAL_NONE",
@@ -40,6 +41,8 @@ __all__ = [
     "fa_forward_f32",
     "fa_decode_splitkv",
     "fa_decode_workspace_bytes",
+    "fa_decode_splitkv_noalloc",
+    "DECODE_NOALLOC_SCRATCH_BYTES",
     "fa_backward",
     "fa_backward_workspace_bytes",
     "fa_status_string",
@@ -82,14 +85,12 @@ def _check_devices(ref: torch.Tensor, **tensors) -> None:
             raise ValueError(f"{name} must live on {ref.device} (got {t.device})")
 
 
-def _check_workspace(workspace, need: int) -> int:
-    """A contiguous tensor of at least ``need`` bytes; returns its size in bytes."""
+def _check_workspace(workspace) -> int:
+    """A contiguous tensor; returns its size in bytes, which the library
+    compares with what the call needs (FA_ERR_INVALID_ARG when short)."""
     if not isinstance(workspace, torch.Tensor) or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous torch.Tensor")
-    nbytes = workspace.numel() * workspace.element_size()
-    if nbytes < need:
-        raise ValueError(f"workspace holds {nbytes} bytes; {need} are needed")
-    return nbytes
+    return workspace.numel() * workspace.element_size()
 
 
 def _causal_mode(causal) -> int:
@@ -211,7 +212,7 @@ def fa_decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, num_spl
     not given."""
     B, H, Nk, D = _check_decode(q, k, v, out, lse, kv_lens)
     need = fa_decode_workspace_bytes(B, H, D, num_splits)
-    ws_bytes = _check_workspace(workspace, need) if workspace is not None else None
+    ws_bytes = _check_workspace(workspace) if workspace is not None else None
     _check_devices(q, k=k, v=v, out=out, lse=lse, kv_lens=kv_lens, workspace=workspace)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
@@ -235,6 +236,29 @@ def fa_decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, num_spl
             q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_p, kv_lens.data_ptr(),
             workspace.data_ptr(), ws_bytes, B, H, Nk, D, float(scale), int(num_splits), _stream(q))
     _lib.check(code, name)
+    return out, lse
+
+
+def fa_decode_splitkv_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, num_splits: int,
+                              out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                              scale: Optional[float] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """bf16 split-KV decode that allocates nothing: the partial states live in
+    the library's fixed per-GPU scratch (DECODE_NOALLOC_SCRATCH_BYTES), so the
+    caller passes the outputs, ``out`` [B,H,1,D] and optionally ``lse`` fp32
+    [B,H]. Calls that may overlap in time on one GPU share that scratch and
+    must be serialised by the caller. Returns (out, lse)."""
+    if not isinstance(q, torch.Tensor) or q.dtype != torch.bfloat16:
+        raise TypeError(f"q must be a bfloat16 tensor (got {getattr(q, 'dtype', type(q))})")
+    if out is None:
+        raise ValueError("out is required: this entry point allocates nothing")
+    B, H, Nk, D = _check_decode(q, k, v, out, lse, None)
+    _check_devices(q, k=k, v=v, out=out, lse=lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    code = _lib.load().fa_decode_splitkv_noalloc(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr() if lse is not None else None,
+        B, H, Nk, D, float(scale), int(num_splits), _stream(q))
+    _lib.check(code, "fa_decode_splitkv_noalloc")
     return out, lse
 
 
@@ -265,7 +289,7 @@ def fa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tens
     _check_kv_lens(kv_lens, B)
     mode = _causal_mode(causal)
     need = fa_backward_workspace_bytes(B, H, Nq)
-    ws_bytes = _check_workspace(workspace, need) if workspace is not None else None
+    ws_bytes = _check_workspace(workspace) if workspace is not None else None
     _check_devices(q, k=k, v=v, o=o, do=do, lse=lse, dq=dq, dk=dk, dv=dv, kv_lens=kv_lens, workspace=workspace)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
@@ -355,7 +379,7 @@ def fa_forward_rope(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cos: torc
     _check_kv_lens(kv_lens, B)
     st, mode = _rope_style(style), _causal_mode(causal)
     need = fa_rope_workspace_bytes(B, H, Nk, D)
-    ws_bytes = _check_workspace(workspace, need) if workspace is not None else None
+    ws_bytes = _check_workspace(workspace) if workspace is not None else None
     _check_devices(q, k=k, v=v, cos=cos, sin=sin, out=out, lse=lse, kv_lens=kv_lens, workspace=workspace)
     if scale is None:
         scale = 1.0 / math.sqrt(D)

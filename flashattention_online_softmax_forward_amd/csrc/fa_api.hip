@@ -9,6 +9,8 @@
 #include "fa.h"
 #include "fa_internal.h"
 
+static_assert(FA_DECODE_NOALLOC_SCRATCH_BYTES == fa::kDecodeScratchBytes,
+              "the header states the size of the decode scratch");
 static_assert(FA_ROPE_HALF == fa::kRopeHalf && FA_ROPE_PAIRS == fa::kRopePairs,
               "RoPE styles of the C ABI and the kernels agree");
 static_assert(FA_CAUSAL_NONE == fa::kCausalNone && FA_CAUSAL_TOP_LEFT == fa::kCausalTopLeft &&
@@ -268,6 +270,21 @@ fa_status fa_decode_splitkv(const void* Q, const void* K, const void* V, void* O
                             float scale, int num_splits, hipStream_t stream) {
     return fa_decode_splitkv_masked(Q, K, V, O, LSE, nullptr, workspace, workspace_bytes, B, H, Nk, D, scale,
                                     num_splits, stream);
+}
+
+fa_status fa_decode_splitkv_noalloc(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
+                                    int H, int Nk, int D, float scale, int num_splits, hipStream_t stream) {
+    if (B < 0 || H < 0 || Nk < 0 || num_splits < 1) return FA_ERR_INVALID_ARG;
+    if (!good_scale(scale)) return FA_ERR_INVALID_ARG;
+    if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * H == 0) return FA_OK;
+    // The partial states must fit the fixed scratch; checked before any HIP call.
+    if (fa_decode_workspace_bytes(B, H, D, num_splits) > FA_DECODE_NOALLOC_SCRATCH_BYTES) return FA_ERR_UNSUPPORTED;
+    if (!Q || !K || !V || !O || Nk < 1) return FA_ERR_INVALID_ARG;
+    void* scratch = nullptr;
+    if (fa::decode_scratch(&scratch) != hipSuccess) return FA_ERR_LAUNCH;
+    return decode_impl(Q, K, V, O, LSE, nullptr, scratch, FA_DECODE_NOALLOC_SCRATCH_BYTES, B, H, Nk, D, scale,
+                       num_splits, stream, false);
 }
 
 size_t fa_backward_workspace_bytes(int B, int H, int Nq) {

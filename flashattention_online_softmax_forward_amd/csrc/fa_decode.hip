@@ -22,6 +22,8 @@
 // kv_lens), split into S chunks of ceil(Lk / S) keys. A cache with no real key
 // has only empty chunks and gets O = 0, LSE = -inf.
 
+#include <mutex>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -237,6 +239,37 @@ static hipError_t launch_d(const DecodeArgs& a) {
 hipError_t launch_decode(const DecodeArgs& a) {
     if (a.f16) return a.D == 128 ? launch_d<_Float16, 128>(a) : launch_d<_Float16, 64>(a);
     return a.D == 128 ? launch_d<__bf16, 128>(a) : launch_d<__bf16, 64>(a);
+}
+
+// Fixed scratch of the allocation-free decode entry point: the partial states
+// (m, l, o) that launch_decode otherwise keeps in a caller's workspace. One
+// copy per GPU, alive until the process ends. Host code must never pass the
+// array's name to a kernel (on the host it is only a stand-in for the
+// symbol): the device address comes from hipGetSymbolAddress, taken once per
+// device with that device current, and is used everywhere instead.
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 }  // namespace fa

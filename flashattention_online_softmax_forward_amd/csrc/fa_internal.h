@@ -93,6 +93,12 @@ hipError_t launch_fwd_f16(const FwdArgs& a);
 hipError_t launch_rope(const RopeArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
+
+// Size of the fixed per-GPU scratch of fa_decode_splitkv_noalloc.
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+// Device address of that scratch on the current device (looked up once per
+// device, then cached).
+hipError_t decode_scratch(void** ptr);
 hipError_t launch_bwd(const BwdArgs& a);
 
 }  // namespace fa

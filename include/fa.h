@@ -236,6 +236,30 @@ fa_status fa_decode_splitkv_f16_masked(const void* Q, const void* K, const void*
                                        float scale, int num_splits, hipStream_t stream);
 
 /*
+ * fa_decode_splitkv without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The partial states live in a fixed scratch
+ * array inside the library, FA_DECODE_NOALLOC_SCRATCH_BYTES bytes per GPU,
+ * held from the first call on a device until the process ends; the call
+ * itself allocates nothing. Arguments, results and errors as
+ * fa_decode_splitkv (bf16), plus:
+ *   - FA_ERR_UNSUPPORTED when fa_decode_workspace_bytes(B,H,D,num_splits)
+ *     exceeds FA_DECODE_NOALLOC_SCRATCH_BYTES (checked before any HIP call);
+ *   - FA_ERR_LAUNCH when the scratch's device address cannot be looked up.
+ *   - `stream` must belong to the calling thread's current device, whose copy
+ *     of the scratch is used.
+ * Every call on one GPU shares that GPU's scratch: calls that may overlap in
+ * time on one GPU (on different streams, or from different threads) race and
+ * must be serialised by the caller. Nothing in the scratch needs clearing:
+ * every call overwrites all the partial states it reads.
+ */
+#define FA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+fa_status fa_decode_splitkv_noalloc(const void* Q, const void* K, const void* V,
+                                    void* O, float* LSE,
+                                    int B, int H, int Nk, int D,
+                                    float scale, int num_splits, hipStream_t stream);
+
+/*
  * Bytes of device workspace fa_backward needs: B*H*Nq*4 (one fp32 value per
  * query row, D_i = sum_d dO[i,d] * O[i,d]). Returns 0 for invalid arguments.
  */

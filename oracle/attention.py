@@ -193,32 +193,30 @@ def softmax_weights(q, k, scale: float, causal=False, kv_len: int | None = None)
 def online_per_key(s, v, trace: bool = False):
     """Online softmax over one score row, one key at a time (section 11.6).
 
-    s: [N] scaled scores; v: [N, Dv] (or [N] for a scalar value). State starts
-    at (m, l, o) = (-inf, 0, 0). For each key j the maximum becomes
-    m_j = max(m_{j-1}, s_j), the old sum and output are multiplied by
-    corr = exp(m_{j-1} - m_j) and the key adds exp(s_j - m_j) (times v_j).
+    s: [N] scaled scores; v: [N, Dv] (or [N] for a scalar value). Key j on its
+    own is the partial state (s_j, 1, v_j): its maximum is its score, its sum
+    e^0 = 1 and its output v_j (a masked score, -inf, is the empty state
+    (-inf, 0, 0)). The row's state is these single-key states folded left to
+    right with ``merge``, starting from the empty state. Each fold rescales
+    the running (l, o) by corr = e^{m - m'} and weighs the new key by
+    p = e^{s_j - m'}, m' = max(m, s_j): the per-key recurrence of the section.
     Returns (m, l, o) and, with ``trace``, the list of per-key states
     (m, corr, p, l, o). The answer is o / l.
     """
     s = _f64(s)
     v = _f64(v)
-    o = np.zeros(v.shape[1:])
-    m, l = NEG_INF, 0.0
+    empty = (NEG_INF, 0.0, np.zeros(v.shape[1:]))
+    state = empty
     states = []
     for j in range(s.shape[0]):
-        m_new = max(m, s[j])
-        # exp(-inf - finite) = 0 multiplies the empty start state; a row whose
-        # every score so far is -inf keeps corr = 1 instead of exp(nan).
-        corr = 1.0 if m_new == NEG_INF else math.exp(m - m_new)
-        p = 0.0 if m_new == NEG_INF else math.exp(s[j] - m_new)
-        l = l * corr + p
-        o = o * corr + p * v[j]
-        m = m_new
+        key_state = empty if s[j] == NEG_INF else (float(s[j]), 1.0, v[j])
+        _, corr, p = _rescale_weights(state[0], key_state[0])
+        state = merge(state, key_state)
         if trace:
-            states.append((m, corr, p, l, np.array(o)))
+            states.append((state[0], corr, p, state[1], np.array(state[2])))
     if trace:
-        return (m, l, o), states
-    return m, l, o
+        return state, states
+    return state
 
 
 def online_blocked(q, k, v, scale: float, causal, block: int, kv_len: int | None = None):
@@ -261,6 +259,17 @@ def online_blocked(q, k, v, scale: float, causal, block: int, kv_len: int | None
     return out, lse
 
 
+def _rescale_weights(m1: float, m2: float):
+    """The common base m = max(m1, m2) of two partial states and the factors
+    e^{m1 - m}, e^{m2 - m} that bring each state onto it. An empty side
+    (m_i = -inf) gets factor 0; when both sides are empty the base stays -inf
+    and the factors are 1 and 0 (nothing to rescale, nothing to add)."""
+    m = max(m1, m2)
+    if m == NEG_INF:
+        return m, 1.0, 0.0
+    return m, math.exp(m1 - m), math.exp(m2 - m)
+
+
 def merge(a, b):
     """Merge two partial states (m, l, o) into the state of the union of their keys.
 
@@ -270,11 +279,9 @@ def merge(a, b):
     """
     m1, l1, o1 = a
     m2, l2, o2 = b
-    m = max(m1, m2)
+    m, w1, w2 = _rescale_weights(m1, m2)
     if m == NEG_INF:
         return (NEG_INF, 0.0, np.zeros_like(_f64(o1)))
-    w1 = math.exp(m1 - m)
-    w2 = math.exp(m2 - m)
     return (m, l1 * w1 + l2 * w2, _f64(o1) * w1 + _f64(o2) * w2)
 
 

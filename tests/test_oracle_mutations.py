@@ -28,11 +28,13 @@ MUTATIONS = {
     "empty_combine_nan": ("    if l == 0.0:                          # every chunk empty: no key at all",
                           "    if False:"),
     "unshifted_exp": ("p = np.exp(s - m)                                 #", "p = np.exp(s)                                     #"),
-    "per_key_forgot_rescale": ("o = o * corr + p * v[j]", "o = o + p * v[j]"),
-    "per_key_l_not_rescaled": ("l = l * corr + p", "l = l + p"),
+    "per_key_state_sum_zero": ("(float(s[j]), 1.0, v[j])", "(float(s[j]), 0.0, v[j])"),
+    "per_key_state_wrong_value": ("(float(s[j]), 1.0, v[j])", "(float(s[j]), 1.0, v[0])"),
+    "rescale_keeps_old_base": ("return m, math.exp(m1 - m), math.exp(m2 - m)", "return m, 1.0, math.exp(m2 - m)"),
     "blocked_forgot_rescale": ("acc = alpha * acc + p @ v[j0:j1]", "acc = acc + p @ v[j0:j1]"),
     "blocked_alpha_sign": ("alpha = math.exp(m - m_new)", "alpha = math.exp(m_new - m)"),
-    "merge_weight_sign": ("w1 = math.exp(m1 - m)", "w1 = math.exp(m - m1)"),
+    "merge_weight_sign": ("return m, math.exp(m1 - m), math.exp(m2 - m)",
+                          "return m, math.exp(m - m1), math.exp(m2 - m)"),
     "merge_drops_second_o": ("o1) * w1 + _f64(o2) * w2)", "o1) * w1)"),
     "chunk_floor": ("c = -(-nk // num_splits)", "c = max(1, nk // num_splits)"),
     "bwd_dv_untransposed": ("dv = p.T @ do", "dv = p @ do"),
