@@ -1,24 +1,41 @@
-"""Benchmark of the MI355X FlashAttention forward library.
+"""Benchmark of the MI355X FlashAttention library: one JSON line.
 
-One step = one ``fa_forward`` call over the prefill workload the metric is
-quoted on (B=1, H=32, Nq=Nk=2048, D=128, bf16, non-causal), inputs already
-resident in HBM. The metric's second half, split-KV decode bandwidth, is
-measured in the same run on the decode workload (B=16, H=32, one query,
-Nk=32768, D=128, 64 splits) and reported under "decode". The backward pass
-(recompute from the saved LSE) is timed on the prefill workload and reported
-under "backward". Prints ONE JSON line.
+The headline step is one ``fa_forward`` call over the prefill workload the
+metric is quoted on (B=1, H=32, Nq=Nk=2048, D=128, bf16, non-causal), inputs
+already resident in HBM. Every other workload the method is checked on is
+timed in the same run, each as a leg of its own with its roofline and an
+oracle baseline beside it:
+  c1        single head, fp32 [1,1,256,64] (launch-bound: time only, no claim)
+  c3        causal prefill [4,32,4096,128], Q and K x3
+  c4        causal prefill [1,16,16000,64] with a ragged tail
+  decode    split-KV decode B=16, H=32, Nk=32768, D=128, 64 splits (two kernels)
+  backward  the backward pass with recompute on the headline workload
 
-Timing: W untimed warm-up steps plus untimed steps until half a second of GPU
-work has run (the engine clock ramps up under load), then K steps between two
-HIP events recorded on the stream the kernels are launched on (torch's current
-stream, which is the stream handed to the library), synchronised on both
-sides.
+Timing: W untimed warm-up calls plus untimed calls until half a second of GPU
+work has run (the engine clock ramps up under load), then K calls between two
+HIP events recorded on the stream the kernels are launched on (torch's
+current stream, which is the stream handed to the library), synchronised on
+both sides.
 
 Algorithmic counts (not the implementation's):
-  prefill FLOPs = 4*B*H*Nq*Nk*D (halved when causal)
-  bytes         = Q, K, V read once + O written once (+ LSE, fp32)
+  forward FLOPs  = 4*B*H*Nq*Nk*D, halved when causal
+  forward bytes  = Q, K, V read once + O written once (+ LSE, fp32)
+  decode bytes   = K, V read once + q read and O written once (+ LSE)
   backward FLOPs = 10*B*H*Nq*Nk*D (S, dP, dV, dQ, dK: five products; halved
                    when causal), the recompute of S counted
+
+Each leg's ``roofline`` carries ``traffic`` (HBM bytes per launch) and, for
+the MFMA kernels, ``mfma_busy`` (the fraction of SIMD cycles in which the
+matrix core was busy) read from the rocprofv3 summary of that kernel and
+workload under profiles/, and only while the kernel's source still has the
+digest recorded there; otherwise they are null.
+
+``cpu_baseline`` (each leg): the fp64 oracle as it stands, on the host, on a
+bounded sample of the leg's own inputs. Samples are independent units (a
+block of query rows of one head; one head for decode and the backward), run
+by one thread per core of the process's affinity mask (at most 16), each with
+a single-threaded BLAS, until the leg's time budget is spent. The rate is the
+algorithmic work of the completed units over the wall time of the run.
 """
 
 from __future__ import annotations
@@ -26,10 +43,10 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
-import math
 import os
 import re
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -41,6 +58,21 @@ PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "flashattention_online_softmax_forward_amd", "csrc")
+MAX_BASELINE_THREADS = 16
+
+HEADLINE = "prefill_b1_h32_n2048_d128"
+# leg -> (workload, what is timed)
+LEGS = {
+    "c1": ("single_head_f32_256x64", "forward"),
+    "c3": ("causal_b4_h32_n4096_d128_qkx3", "forward"),
+    "c4": ("causal_b1_h16_n16000_d64", "forward"),
+    "decode": ("decode_b16_h32_kv32768_d128_s64", "decode"),
+    "backward": (HEADLINE, "backward"),
+}
+FWD_FILES = ["fa_fwd_mfma.hip", "fa_device.h", "fa_internal.h"]
+F32_FILES = ["fa_fwd_f32.hip", "fa_device.h", "fa_internal.h"]
+DEC_FILES = ["fa_decode.hip", "fa_device.h", "fa_internal.h"]
+BWD_FILES = ["fa_bwd.hip", "fa_device.h", "fa_internal.h"]
 
 
 def _code_only(text):
@@ -59,18 +91,23 @@ def kernel_source_digest(files):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(name, digest):
-    """HBM bytes per launch recorded from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
-    in profiles/<name>.md, or None when absent or taken on other kernel source."""
+def profile_value(name, key, digest):
+    """``key: value`` recorded in profiles/<name>.md from rocprofv3 counter
+    runs, or None when absent or taken on other kernel source."""
     path = os.path.join(PROFILES, name + ".md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_src = re.search(r"kernel_source_digest:\s*([0-9a-f]+)", text)
-    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_src or not m_b or m_src.group(1) != digest:
+    m_v = re.search(r"^" + re.escape(key) + r":\s*([0-9.eE+-]+)\s*$", text, flags=re.M)
+    if not m_src or not m_v or m_src.group(1) != digest:
         return None
-    return float(m_b.group(1))
+    return float(m_v.group(1))
+
+
+def measured_traffic(name, digest):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated) of profiles/<name>.md."""
+    return profile_value(name, "hbm_bytes_per_launch", digest)
 
 
 def workload_counts(w):
@@ -104,58 +141,202 @@ def time_steps(fn, steps, warmup, torch, settle_s=0.5):
     return start.elapsed_time(end) / steps
 
 
-def cpu_baseline(w, q, k, v, budget_s):
-    """The fp64 oracle as it stands, on the host, over whole heads of the same
-    workload until about ``budget_s`` seconds of work are done."""
+# ---------------------------------------------------------------- oracle baseline
+
+def baseline_threads():
+    return max(1, min(len(os.sched_getaffinity(0)), MAX_BASELINE_THREADS))
+
+
+def run_units(units, budget_s, threads):
+    """Run ``units`` (callables returning their algorithmic work) round robin
+    on ``threads`` threads until ``budget_s`` seconds have passed; a unit that
+    has started is finished. Returns (completed units, total work, wall s)."""
+    lock = threading.Lock()
+    state = {"next": 0, "done": 0, "work": 0.0}
+    t0 = time.perf_counter()
+    deadline = t0 + budget_s
+
+    def worker():
+        while time.perf_counter() < deadline:
+            with lock:
+                i = state["next"]
+                state["next"] += 1
+            w = units[i % len(units)]()
+            with lock:
+                state["done"] += 1
+                state["work"] += w
+    pool = [threading.Thread(target=worker) for _ in range(threads)]
+    for t in pool:
+        t.start()
+    for t in pool:
+        t.join()
+    return state["done"], state["work"], time.perf_counter() - t0
+
+
+def _widen(t, np):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def cpu_baseline(kind, w, tensors, budget_s, max_bytes=4 << 30):
+    """The fp64 oracle as it stands on a bounded sample of one leg's inputs.
+
+    kind "forward": units of up to 512 query rows of one head, through
+    ``attention_rows``; work = 4 D sum_i (keys row i may see), in FLOP.
+    kind "decode": one head per unit, through ``decode``; work = the head's
+    algorithmic bytes. kind "backward": one head per unit, through
+    ``attention_backward_head``; work = 10 Nq Nk D FLOP (halved causal).
+    At most ``max_bytes`` of widened fp64 inputs are prepared (heads in
+    order); the units cycle over them until the budget is spent."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_limits
 
     from oracle import attention as orc
 
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
-    flops_head = 4.0 * w.Nq * w.Nk * w.D * (0.5 if w.causal else 1.0)
-    done, t_total, passes = 0, 0.0, 0
-    widened = {}
-    # Whole heads in order, over and over (the workload is one pass) until the
-    # budget is spent; only the oracle call itself is timed.
-    while t_total < budget_s:
-        for (b, h) in heads:
-            if (b, h) not in widened:
-                widened[(b, h)] = tuple(x[b, h].float().cpu().numpy().astype(np.float64)[None, None]
-                                        for x in (q, k, v))
-            qh, kh, vh = widened[(b, h)]
-            t0 = time.perf_counter()
-            orc.attention(qh, kh, vh, w.scale, w.causal)
-            t_total += time.perf_counter() - t0
-            done += 1
-            if t_total >= budget_s:
-                break
-        passes += 1
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    per_head = 8 * sum(t[0, 0].numel() for t in tensors)
+    heads = heads[:max(1, min(len(heads), max_bytes // per_head))]
+    # Widened before the clock starts: the oracle is timed, not the copies.
+    wide = {bh: tuple(_widen(t[bh[0], bh[1]], np) for t in tensors) for bh in heads}
+
+    units = []
+    if kind == "forward":
+        rows_per_unit = min(w.Nq, 512)
+        for bh in heads:
+            for r0 in range(0, w.Nq, rows_per_unit):
+                rows = np.arange(r0, min(w.Nq, r0 + rows_per_unit))
+                seen = np.minimum(rows + 1, w.Nk) if w.causal else np.full(rows.shape, w.Nk)
+                work = 4.0 * w.D * float(seen.sum())
+
+                def unit(bh=bh, rows=rows, work=work):
+                    q, k, v = wide[bh]
+                    orc.attention_rows(q[rows], rows, k, v, w.scale, w.causal, nq=w.Nq)
+                    return work
+                units.append(unit)
+        unit_desc, unit_name, scale_to = f"{rows_per_unit}-row blocks", "TFLOP/s", 1e12
+    elif kind == "decode":
+        work = 2.0 * (2 * w.Nk * w.D + 2 * w.D) + 4.0
+        for bh in heads:
+            def unit(bh=bh):
+                q, k, v = wide[bh]
+                orc.decode(q[None, None], k[None, None], v[None, None], w.scale)
+                return work
+            units.append(unit)
+        unit_desc, unit_name, scale_to = "heads", "GB/s", 1e9
+    else:
+        work = 10.0 * w.Nq * w.Nk * w.D * (0.5 if w.causal else 1.0)
+        for bh in heads:
+            def unit(bh=bh):
+                q, k, v, do = wide[bh]
+                orc.attention_backward_head(q, k, v, do, w.scale, w.causal)
+                return work
+            units.append(unit)
+        unit_desc, unit_name, scale_to = "heads", "TFLOP/s", 1e12
+
+    threads = baseline_threads()
+    with threadpool_limits(limits=1):
+        done, total, wall = run_units(units, budget_s, threads)
     return {
-        "value": flops_head * done / t_total / 1e12,
-        "unit": "TFLOP/s",
-        "cores": int(threads),
+        "value": total / wall / scale_to,
+        "unit": unit_name,
+        "cores": threads,
         "kind": "oracle",
-        "sample": f"{done} head computations ({done / len(heads):.2f} passes over the {len(heads)} heads) of "
-                  f"{w.name}, fp64 two-pass, every row, {t_total:.1f} s",
+        "sample": f"{done} units ({unit_desc}, cycling over {len(units)} units of the first {len(heads)} of "
+                  f"{w.B * w.H} heads) of {w.name}, fp64 two-pass oracle, {wall:.1f} s wall on {threads} threads "
+                  f"(one per core of the affinity mask, single-threaded BLAS each)",
     }
+
+
+# ---------------------------------------------------------------- legs
+
+def roofline(kernel, bound, achieved, peak, unit, profile, digest, mfma):
+    r = {"kernel": kernel, "bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 4), "traffic": measured_traffic(profile, digest),
+         "kernel_source_digest": digest}
+    if mfma:
+        r["mfma_busy"] = profile_value(profile, "mfma_busy", digest)
+    return r
+
+
+def forward_leg(fa, synth, torch, w, steps, warmup):
+    q, k, v = synth.make_workload(w, seed=0, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+    if w.dtype == torch.float32:
+        step = lambda: fa.fa_forward_f32(q, k, v, causal=w.causal, scale=w.scale, out=out, lse=lse)  # noqa: E731
+        kname, peak, files, dtype = "fwd_f32_kernel", PEAK_FP32_TFLOPS, F32_FILES, "f32"
+    else:
+        step = lambda: fa.fa_forward(q, k, v, causal=w.causal, scale=w.scale, out=out, lse=lse)  # noqa: E731
+        kname, peak, files, dtype = "fwd_mfma_kernel", PEAK_BF16_TFLOPS, FWD_FILES, "bf16"
+    ms = time_steps(step, steps, warmup, torch)
+    flops, bytes_ = workload_counts(w)
+    tflops = flops / (ms * 1e-3) / 1e12
+    digest = kernel_source_digest(files)
+    leg = {
+        "workload": w.name, "dtype": dtype, "ms_per_call": round(ms, 6), "value": round(tflops, 3),
+        "unit": "TFLOP/s", "algorithmic_flops": flops, "algorithmic_bytes": bytes_,
+        "config": {"B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "D": w.D, "causal": w.causal,
+                   "qk_mul": w.qk_mul, "scale": w.scale},
+        "roofline": roofline(kname, "mfma" if dtype == "bf16" else "alu", tflops, peak, "TFLOP/s",
+                             f"{kname}_{w.name}", digest, dtype == "bf16"),
+    }
+    return leg, (q, k, v)
+
+
+def decode_leg(fa, synth, torch, w, steps, warmup):
+    q, k, v = synth.make_workload(w, seed=0, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(fa.fa_decode_workspace_bytes(w.B, w.H, w.D, w.num_splits), dtype=torch.uint8, device="cuda")
+    step = lambda: fa.fa_decode_splitkv(q, k, v, w.num_splits, scale=w.scale, workspace=ws,  # noqa: E731
+                                        out=out, lse=lse)
+    ms = time_steps(step, steps, warmup, torch)
+    _, bytes_ = workload_counts(w)
+    gbs = bytes_ / (ms * 1e-3) / 1e9
+    digest = kernel_source_digest(DEC_FILES)
+    leg = {
+        "workload": w.name, "ms_per_call": round(ms, 6), "value": round(gbs, 2), "unit": "GB/s",
+        "algorithmic_bytes": bytes_, "num_splits": w.num_splits,
+        "roofline": roofline("decode_partial_kernel + decode_combine_kernel", "hbm", gbs, PEAK_HBM_GBS, "GB/s",
+                             f"decode_partial_kernel_{w.name}", digest, False),
+    }
+    return leg, (q, k, v)
+
+
+def backward_leg(fa, synth, torch, w, steps, warmup):
+    if w.dtype != torch.bfloat16 or w.is_decode:
+        raise SystemExit("the backward leg is bf16 prefill only")
+    q, k, v = synth.make_workload(w, seed=0, device="cuda")
+    do = synth.make_do(w.B, w.H, w.Nq, w.D, w.dtype, seed=0, device="cuda")
+    o, lse = fa.fa_forward(q, k, v, causal=w.causal, scale=w.scale)
+    grads = tuple(torch.empty_like(t) for t in (q, k, v))
+    ws = torch.empty(max(16, fa.fa_backward_workspace_bytes(w.B, w.H, w.Nq)), dtype=torch.uint8, device="cuda")
+    step = lambda: fa.fa_backward(q, k, v, o, do, lse, causal=w.causal, scale=w.scale,  # noqa: E731
+                                  workspace=ws, dq=grads[0], dk=grads[1], dv=grads[2])
+    ms = time_steps(step, steps, warmup, torch)
+    fwd_flops, _ = workload_counts(w)
+    flops = 2.5 * fwd_flops
+    tf = flops / (ms * 1e-3) / 1e12
+    digest = kernel_source_digest(BWD_FILES)
+    leg = {
+        "workload": w.name, "ms_per_call": round(ms, 6), "value": round(tf, 3), "unit": "TFLOP/s",
+        "algorithmic_flops": flops,
+        "roofline": roofline("bwd_dq_kernel + bwd_dkdv_kernel", "mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s",
+                             f"bwd_kernels_{w.name}", digest, True),
+    }
+    return leg, (q, k, v, do)
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=200, help="timed calls of the headline step")
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="prefill_b1_h32_n2048_d128")
-    ap.add_argument("--decode-workload", default="decode_b16_h32_kv32768_d128_s64")
-    ap.add_argument("--decode-steps", type=int, default=50)
-    ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--backward-workload", default=None, help="default: --workload")
-    ap.add_argument("--backward-steps", type=int, default=50)
-    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--leg-steps", type=int, default=50, help="timed calls of every other leg")
+    ap.add_argument("--legs", default=",".join(LEGS), help="comma-separated subset of: " + ", ".join(LEGS))
+    ap.add_argument("--workload", default=HEADLINE, help="headline workload (a prefill workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work, headline leg")
+    ap.add_argument("--leg-cpu-budget", type=float, default=5.0, help="seconds of oracle work, other legs")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of attention, time a plain device copy of this many bytes "
                          "(calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -165,6 +346,10 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the library runs on a single GPU; there is no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
+    legs = [x for x in args.legs.split(",") if x]
+    for x in legs:
+        if x not in LEGS:
+            raise SystemExit(f"unknown leg {x!r}; choose from {', '.join(LEGS)}")
 
     import torch
 
@@ -184,98 +369,49 @@ def main():
         return
 
     w = synth.WORKLOADS[args.workload]
-    q, k, v = synth.make_workload(w, seed=0, device="cuda")
-    out = torch.empty_like(q)
-    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
-    if w.is_decode:
-        raise SystemExit("--workload names a prefill workload; decode is reported under 'decode'")
-    if w.dtype == torch.float32:
-        step = lambda: fa.fa_forward_f32(q, k, v, causal=w.causal, scale=w.scale, out=out, lse=lse)  # noqa: E731
-        peak, dtype, kname = PEAK_FP32_TFLOPS, "f32", "fwd_f32_kernel"
-        files = ["fa_fwd_f32.hip", "fa_device.h", "fa_internal.h"]
-    else:
-        step = lambda: fa.fa_forward(q, k, v, causal=w.causal, scale=w.scale, out=out, lse=lse)  # noqa: E731
-        peak, dtype, kname = PEAK_BF16_TFLOPS, "bf16", "fwd_mfma_kernel"
-        files = ["fa_fwd_mfma.hip", "fa_device.h", "fa_internal.h"]
-    ms = time_steps(step, args.steps, args.warmup, torch)
-    flops, _ = workload_counts(w)
-    tflops = flops / (ms * 1e-3) / 1e12
-    digest = kernel_source_digest(files)
-    traffic = measured_traffic(f"{kname}_{w.name}", digest)
-
+    if w.is_decode or w.dtype != torch.bfloat16:
+        raise SystemExit("--workload names the bf16 prefill workload of the headline step")
+    head, head_inputs = forward_leg(fa, synth, torch, w, args.steps, args.warmup)
+    print(f"[bench] {w.name}: {head['ms_per_call']:.6f} ms, {head['value']:.1f} TFLOP/s", file=sys.stderr,
+          flush=True)
     result = {
         "metric": METRIC,
-        "value": round(tflops, 3),
+        "value": head["value"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 6),
+        "ms_per_step": head["ms_per_call"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dtype,
+        "dtype": "bf16",
         "data": "synthetic (seeded i.i.d. N(0,1) inputs)",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "D": w.D,
-                   "causal": w.causal, "scale": w.scale},
-        "roofline": {"kernel": kname, "bound": "mfma", "achieved": round(tflops, 3), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic,
-                     "kernel_source_digest": digest},
+        "config": dict(workload=w.name, **head["config"]),
+        "roofline": head["roofline"],
     }
 
-    if not args.no_decode:
-        dw = synth.WORKLOADS[args.decode_workload]
-        dq, dk, dv = synth.make_workload(dw, seed=0, device="cuda")
-        dout = torch.empty_like(dq)
-        dlse = torch.empty((dw.B, dw.H), dtype=torch.float32, device="cuda")
-        ws = torch.empty(fa.fa_decode_workspace_bytes(dw.B, dw.H, dw.D, dw.num_splits), dtype=torch.uint8,
-                         device="cuda")
-        dstep = lambda: fa.fa_decode_splitkv(dq, dk, dv, dw.num_splits, scale=dw.scale, workspace=ws,  # noqa: E731
-                                             out=dout, lse=dlse)
-        dms = time_steps(dstep, args.decode_steps, args.warmup, torch)
-        _, dbytes = workload_counts(dw)
-        gbs = dbytes / (dms * 1e-3) / 1e9
-        ddigest = kernel_source_digest(["fa_decode.hip", "fa_device.h", "fa_internal.h"])
-        result["decode"] = {
-            "workload": dw.name, "ms_per_call": round(dms, 6), "value": round(gbs, 2), "unit": "GB/s",
-            "algorithmic_bytes": dbytes, "num_splits": dw.num_splits,
-            "roofline": {"kernel": "decode_partial_kernel + decode_combine_kernel", "bound": "hbm",
-                         "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": measured_traffic(f"decode_partial_kernel_{dw.name}", ddigest),
-                         "kernel_source_digest": ddigest},
-        }
-        del dq, dk, dv, ws
+    run = {"forward": forward_leg, "decode": decode_leg, "backward": backward_leg}
+    leg_inputs = {}
+    for name in legs:
+        wname, kind = LEGS[name]
+        lw = synth.WORKLOADS[wname]
+        leg, inputs = run[kind](fa, synth, torch, lw, args.leg_steps, args.warmup)
+        print(f"[bench] {name} {lw.name}: {leg['ms_per_call']:.6f} ms, {leg['value']} {leg['unit']}",
+              file=sys.stderr, flush=True)
+        result[name] = leg
+        if not args.no_cpu_baseline:
+            leg_inputs[name] = (kind, lw, inputs)
+        del inputs
 
-    if not args.no_backward:
-        bw = synth.WORKLOADS[args.backward_workload or args.workload]
-        if bw.dtype != torch.bfloat16 or bw.is_decode:
-            raise SystemExit("the backward pass is bf16 prefill only")
-        bq, bk, bv = synth.make_workload(bw, seed=0, device="cuda")
-        bdo = synth.make_do(bw.B, bw.H, bw.Nq, bw.D, bw.dtype, seed=0, device="cuda")
-        bo, blse = fa.fa_forward(bq, bk, bv, causal=bw.causal, scale=bw.scale)
-        grads = tuple(torch.empty_like(t) for t in (bq, bk, bv))
-        bws = torch.empty(max(16, fa.fa_backward_workspace_bytes(bw.B, bw.H, bw.Nq)), dtype=torch.uint8,
-                          device="cuda")
-        bstep = lambda: fa.fa_backward(bq, bk, bv, bo, bdo, blse, causal=bw.causal, scale=bw.scale,  # noqa: E731
-                                       workspace=bws, dq=grads[0], dk=grads[1], dv=grads[2])
-        bms = time_steps(bstep, args.backward_steps, args.warmup, torch)
-        fwd_flops, _ = workload_counts(bw)
-        btf = 2.5 * fwd_flops / (bms * 1e-3) / 1e12
-        bdigest = kernel_source_digest(["fa_bwd.hip", "fa_device.h", "fa_internal.h"])
-        result["backward"] = {
-            "workload": bw.name, "ms_per_call": round(bms, 6), "value": round(btf, 3), "unit": "TFLOP/s",
-            "algorithmic_flops": 2.5 * fwd_flops,
-            "roofline": {"kernel": "bwd_dq_kernel + bwd_dkdv_kernel", "bound": "mfma",
-                         "achieved": round(btf, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(btf / PEAK_BF16_TFLOPS, 4),
-                         "traffic": measured_traffic(f"bwd_kernels_{bw.name}", bdigest),
-                         "kernel_source_digest": bdigest},
-        }
-        del bq, bk, bv, bdo, bo, grads, bws
-
+    # The oracle runs after every GPU leg, on the host, each leg on its own
+    # inputs (only the heads it samples are copied back).
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline("forward", w, head_inputs, args.cpu_budget)
+        for name, (kind, lw, inputs) in leg_inputs.items():
+            result[name]["cpu_baseline"] = cpu_baseline(kind, lw, inputs, args.leg_cpu_budget)
+            print(f"[bench] {name} oracle: {result[name]['cpu_baseline']['value']:.4g} "
+                  f"{result[name]['cpu_baseline']['unit']}", file=sys.stderr, flush=True)
     print(json.dumps(result), flush=True)
 
 

@@ -56,3 +56,45 @@ def test_profile_traffic_lookup(bench):
         assert bench.measured_traffic(stem, "0" * 16) is None
     assert found >= 3
     assert bench.measured_traffic("no_such_kernel_no_such_workload", "0" * 16) is None
+
+
+def test_profile_value_is_digest_gated(bench, tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    (tmp_path / "k_w.md").write_text("# x\n\nkernel_source_digest: 00ff\nhbm_bytes_per_launch: 123\n"
+                                     "mfma_busy: 0.5125\n")
+    assert bench.profile_value("k_w", "mfma_busy", "00ff") == 0.5125
+    assert bench.profile_value("k_w", "hbm_bytes_per_launch", "00ff") == 123.0
+    assert bench.profile_value("k_w", "mfma_busy", "00fe") is None
+    assert bench.profile_value("k_w", "no_such_key", "00ff") is None
+
+
+def test_run_units_counts_only_completed_work(bench):
+    calls = []
+
+    def unit():
+        calls.append(1)
+        return 2.5
+    done, work, wall = bench.run_units([unit, unit, unit], 0.05, 3)
+    assert done == len(calls) >= 3
+    assert work == 2.5 * done
+    assert wall >= 0.05
+
+
+@pytest.mark.parametrize("kind,name", [("forward", "single_head_f32_256x64"),
+                                       ("forward", "causal_b1_h16_n16000_d64"),
+                                       ("decode", "decode_b16_h32_kv32768_d128_s64"),
+                                       ("backward", "prefill_b1_h32_n2048_d128")])
+def test_cpu_baseline_on_small_stand_ins(bench, kind, name):
+    """The oracle baseline runs on CPU tensors of a workload's layout (shrunk so
+    the test is quick) and reports a positive rate, its unit and its cores."""
+    import dataclasses
+
+    w = synth.WORKLOADS[name]
+    small = dataclasses.replace(w, B=1, H=2, Nq=min(w.Nq, 64), Nk=min(w.Nk, 100))
+    q, k, v = synth.make_workload(small, seed=0)
+    tensors = (q, k, v) if kind != "backward" else (q, k, v, synth.make_do(1, 2, small.Nq, small.D, small.dtype))
+    r = bench.cpu_baseline(kind, small, tensors, 0.2)
+    assert r["value"] > 0 and r["kind"] == "oracle"
+    assert r["unit"] == ("GB/s" if kind == "decode" else "TFLOP/s")
+    assert 1 <= r["cores"] <= bench.MAX_BASELINE_THREADS
+    assert r["cores"] <= len(os.sched_getaffinity(0))
