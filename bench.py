@@ -8,6 +8,8 @@ oracle baseline beside it:
   c1        single head, fp32 [1,1,256,64] (launch-bound: time only, no claim)
   c3        causal prefill [4,32,4096,128], Q and K x3
   c4        causal prefill [1,16,16000,64] with a ragged tail
+  long      non-causal prefill [1,32,16384,128] (beyond the five workloads:
+            the long-sequence end of the non-causal D = 128 regime)
   decode    split-KV decode B=16, H=32, Nk=32768, D=128, 64 splits (two kernels)
   backward  the backward pass with recompute on the headline workload
 
@@ -66,6 +68,7 @@ LEGS = {
     "c1": ("single_head_f32_256x64", "forward"),
     "c3": ("causal_b4_h32_n4096_d128_qkx3", "forward"),
     "c4": ("causal_b1_h16_n16000_d64", "forward"),
+    "long": ("prefill_b1_h32_n16384_d128", "forward"),
     "decode": ("decode_b16_h32_kv32768_d128_s64", "decode"),
     "backward": (HEADLINE, "backward"),
 }

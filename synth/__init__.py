@@ -48,7 +48,7 @@ class Workload:
         return self.num_splits > 0
 
 
-# The five workloads the method is measured and checked on.
+# The workloads the method is measured and checked on.
 WORKLOADS = {
     w.name: w
     for w in [
@@ -59,6 +59,10 @@ WORKLOADS = {
         Workload("causal_b1_h16_n16000_d64", 1, 16, 16000, 16000, 64, torch.bfloat16, causal=True),
         Workload("decode_b16_h32_kv32768_d128_s64", 16, 32, 1, 32768, 128, torch.bfloat16,
                  num_splits=64),
+        # Beyond the five: a long non-causal prefill, the long-sequence end of
+        # the non-causal D = 128 prefill regime (the forward rate grows with N
+        # as each workgroup's Q load and O store are spread over more tiles).
+        Workload("prefill_b1_h32_n16384_d128", 1, 32, 16384, 16384, 128, torch.bfloat16),
     ]
 }
 

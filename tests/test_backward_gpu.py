@@ -110,9 +110,11 @@ def test_backward_matches_oracle(fa, case):
 @pytest.mark.parametrize("name,heads", [
     ("prefill_b1_h32_n2048_d128", [(0, 0), (0, 13), (0, 31)]),
     ("causal_b4_h32_n4096_d128_qkx3", [(0, 0), (3, 31)]),
+    ("causal_b1_h16_n16000_d64", [(0, 15)]),
 ])
 def test_backward_workload_sizes(fa, name, heads):
-    """The measured prefill shapes, every element of a few sampled heads."""
+    """The measured prefill shapes, every element of a few sampled heads (one
+    head at 16000, whose oracle and bounds take about a minute on the host)."""
     w = synth.WORKLOADS[name]
     print(f"[case] bwd workload {name} heads {heads}", flush=True)
     q, k, v = synth.make_workload(w, seed=22)

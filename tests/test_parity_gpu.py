@@ -207,8 +207,11 @@ def test_ones_values_and_causal_first_row(fa):
         assert np.abs(f64(o) - 1.0).max() <= 2.0 ** -8, "V = 1 must give O = 1"
     o, _ = fa.fa_forward(q.to(DEV), k.to(DEV), v.to(DEV), causal=True)
     torch.cuda.synchronize()
-    # row 0 attends key 0 only: O = V[0] up to one bf16 rounding
-    assert np.abs(f64(o)[:, :, 0] - f64(v)[:, :, 0]).max() <= 2.0 ** -8 * np.abs(f64(v)[:, :, 0]).max()
+    # Row 0 attends key 0 only. Its running maximum becomes its own scaled
+    # score, so its one weight is exp2 of that score's fp32 rounding error: a
+    # few fp32 ulps from 1, which bf16 rounds to exactly 1. Then O = V[0] / l
+    # with l that close to 1, and rounding to bf16 gives V[0] back, bit for bit.
+    assert torch.equal(o[:, :, 0].cpu(), v[:, :, 0])
     ofull, _ = fa.fa_forward(q.to(DEV), k.to(DEV), v.to(DEV), causal=False)
     torch.cuda.synchronize()
     # the last row sees every key: causal and full agree bit for bit
