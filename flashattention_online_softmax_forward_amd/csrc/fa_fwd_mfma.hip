@@ -290,6 +290,14 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     };
     float m_pre = kNoKeyMax;   // tile maximum taken by the MFMA step (kMaxInMfma)
     auto step_mfma = [&](int t, const uint16_t* kb, const uint16_t* vb_prev) __attribute__((always_inline)) {
+        // lgkmcnt(0): nothing LDS-side is pending here (the barrier before
+        // this step drained it), but a scalar load of a kernel argument used
+        // only after the loop may be, on the first entry. Scalar loads return
+        // out of order, so while one may be pending the compiler can only
+        // wait for an operand with lgkmcnt(0), i.e. for every operand read
+        // issued ahead. Waiting here once lets the first MFMA of the step
+        // wait for its own operand alone.
+        __builtin_amdgcn_s_waitcnt(0xC07F);
         __builtin_amdgcn_s_setprio(1);
         const bool do_pv = t >= 1 && t - 1 < my_tiles;
         const bool do_qk = t < my_tiles;
