@@ -350,6 +350,19 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
         }
         const int kv0 = t * kBT;
         const bool edge = kv0 + kBT > Lk || (CAUSAL && kv0 + kBT - 1 > wrow0 + doff);
+        // P in place (register r is key 16*(r/8) + 8*h + r%8 of the tile),
+        // then the mask of an edge tile in one branch: a per-score branch
+        // would cut the exponentials into one basic block each, so no two of
+        // them could overlap (measured 670 cycles per tile for this phase).
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = exp2_hw(__builtin_fmaf(s[r], scale2, -l2));
+        if (edge) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = kv0 + (r / 8) * 16 + h * 8 + r % 8;
+                if (key >= Lk || (CAUSAL && key > qrow + doff)) s[r] = 0.f;
+            }
+        }
         V8 dsf[2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -357,12 +370,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int r = tt * 8 + e;
-                float p = exp2_hw(__builtin_fmaf(s[r], scale2, -l2));
-                if (edge) {
-                    const int key = kv0 + tt * 16 + h * 8 + e;
-                    if (key >= Lk || (CAUSAL && key > qrow + doff)) p = 0.f;
-                }
-                ds[e] = p * (dp[r] - dr);
+                ds[e] = s[r] * (dp[r] - dr);
             }
             u32x4_t w;
             w[0] = Elem<T>::pack2(ds[0], ds[1]);
@@ -529,21 +537,28 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
         const bool edge = q0 + kBT > Nq || kw0 + 32 > Lk || (CAUSAL && q0 + doff < kw0 + 31);
         // P (fp32, kept for dS) and its bf16 copy. Register r of lane (j, h)
         // is query 16*(r/8) + 8*h + r%8 of the tile.
-        V8 pf[2];
+        // P in place, then the mask of an edge tile in one branch (a
+        // per-score branch would cut the exponentials into one basic block
+        // each, so no two of them could overlap: measured 818 cycles per tile
+        // for this phase).
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             const f32x4_t la = *(const f32x4_t*)&ld_lds[buf][tt * 16 + h * 8];
             const f32x4_t lb = *(const f32x4_t*)&ld_lds[buf][tt * 16 + h * 8 + 4];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int r = tt * 8 + e;
-                float p = exp2_hw(__builtin_fmaf(s[r], scale2, -(e < 4 ? la[e] : lb[e - 4])));
-                if (edge) {
-                    const int q = q0 + tt * 16 + h * 8 + e;
-                    if (q >= Nq || krow >= Lk || (CAUSAL && q + doff < krow)) p = 0.f;
-                }
-                s[r] = p;
+            for (int e = 0; e < 8; ++e)
+                s[tt * 8 + e] = exp2_hw(__builtin_fmaf(s[tt * 8 + e], scale2, -(e < 4 ? la[e] : lb[e - 4])));
+        }
+        if (edge) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int q = q0 + (r / 8) * 16 + h * 8 + r % 8;
+                if (q >= Nq || krow >= Lk || (CAUSAL && q + doff < krow)) s[r] = 0.f;
             }
+        }
+        V8 pf[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
             u32x4_t w;
             w[0] = Elem<T>::pack2(s[tt * 8 + 0], s[tt * 8 + 1]);
             w[1] = Elem<T>::pack2(s[tt * 8 + 2], s[tt * 8 + 3]);
