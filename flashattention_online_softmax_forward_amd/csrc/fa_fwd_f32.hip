@@ -3,14 +3,17 @@
 // The same tiled online-softmax recurrence as the bf16 kernel (iThome article,
 // "three states"; ML compiler page, section 11.9), in the precision of the FA2
 // kernel sketch on "Kernel visualization: Flash Attention 2", on the vector
-// ALUs: a workgroup of 256 threads owns 64 query rows; 4 threads share a row.
-// Q, the K and V tiles and the P tile sit in LDS; each thread computes 16
-// scores of its row, the row max / sum are reduced over the 4 threads with DPP,
-// and each thread accumulates a quarter of the row's output (D/4 values in
-// VGPRs). Base-2 exponentials with log2(e) folded into the scale. Masks as in
-// the bf16 kernel: key padding (kv_lens), top-left or bottom-right causal
-// alignment (one diagonal offset), and rows with no visible key written as
-// O = 0, LSE = -inf (the running maximum starts finite, kNoKeyMax).
+// ALUs: a workgroup of 256 threads owns 16 query rows and 16 threads share a
+// row, so a single head of 256 rows already spreads over 16 workgroups (with
+// 64 rows per workgroup it ran on 4 CUs, each wave issue-bound on its own
+// share). Q, the K and V tiles and the P tile sit in LDS; each thread computes
+// 4 scores of its row per 64-key tile, the row max / sum are reduced over the
+// 16 threads with DPP, and each thread accumulates D/16 values of the row's
+// output in VGPRs. Base-2 exponentials with log2(e) folded into the scale.
+// Masks as in the bf16 kernel: key padding (kv_lens), top-left or
+// bottom-right causal alignment (one diagonal offset), and rows with no
+// visible key written as O = 0, LSE = -inf (the running maximum starts
+// finite, kNoKeyMax).
 
 #include "fa_device.h"
 #include "fa_internal.h"
@@ -18,7 +21,9 @@
 namespace fa {
 
 constexpr int kF32Threads = 256;
-constexpr int kF32BN = 64;
+constexpr int kF32TPR = 16;            // threads per query row
+constexpr int kF32BN = 64;             // keys per tile
+static_assert(BM_FWD_F32 * kF32TPR == kF32Threads, "one row per 16 threads");
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kF32Threads)
@@ -28,9 +33,11 @@ void fwd_f32_kernel(const float* __restrict__ Qg, const float* __restrict__ Kg,
                     int nqb, float scale2, int bottom_right) {
     constexpr int BM = BM_FWD_F32;
     constexpr int BN = kF32BN;
+    constexpr int TPR = kF32TPR;
     constexpr int P = D + 4;           // row pitch of Q/K/V tiles (floats)
     constexpr int PP = BN + 4;         // row pitch of the P tile
-    constexpr int NE = D / 16;         // float4 output chunks per thread
+    constexpr int NS = BN / TPR;       // scores per thread and tile: keys sub + TPR*i
+    constexpr int NE = D / (4 * TPR);  // float4 output chunks per thread: columns 4*sub + 4*TPR*e
     constexpr int C4 = D / 4;          // float4 chunks per row
 
     __shared__ __attribute__((aligned(16))) float Qs[BM * P];
@@ -39,8 +46,8 @@ void fwd_f32_kernel(const float* __restrict__ Qg, const float* __restrict__ Kg,
     __shared__ __attribute__((aligned(16))) float Ps[BM * PP];
 
     const int tid = threadIdx.x;
-    const int r = tid >> 2;            // query row within the block
-    const int sub = tid & 3;           // quarter of the row
+    const int r = tid / TPR;           // query row within the block
+    const int sub = tid % TPR;         // the thread's share of the row
 
     const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
     const int bh = logical / nqb;
@@ -70,7 +77,7 @@ void fwd_f32_kernel(const float* __restrict__ Qg, const float* __restrict__ Kg,
 #pragma unroll
     for (int e = 0; e < NE; ++e) o[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m_run = kNoKeyMax;
-    float l_run = 0.f;                 // this thread's quarter of the row sum
+    float l_run = 0.f;                 // this thread's share of the row sum
 
     for (int t = 0; t < ntiles; ++t) {
         const int kv0 = t * BN;
@@ -88,15 +95,15 @@ void fwd_f32_kernel(const float* __restrict__ Qg, const float* __restrict__ Kg,
         }
         __syncthreads();
 
-        // Scores of keys sub + 4*i.
-        float s[16];
+        float s[NS];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] = 0.f;
+        for (int i = 0; i < NS; ++i) s[i] = 0.f;
+#pragma unroll 4
         for (int k = 0; k < D; k += 4) {
             const f32x4_t qv = *(const f32x4_t*)(Qs + r * P + k);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const f32x4_t kv = *(const f32x4_t*)(Ks + (sub + 4 * i) * P + k);
+            for (int i = 0; i < NS; ++i) {
+                const f32x4_t kv = *(const f32x4_t*)(Ks + (sub + TPR * i) * P + k);
                 s[i] = __builtin_fmaf(qv[0], kv[0], s[i]);
                 s[i] = __builtin_fmaf(qv[1], kv[1], s[i]);
                 s[i] = __builtin_fmaf(qv[2], kv[2], s[i]);
@@ -105,32 +112,33 @@ void fwd_f32_kernel(const float* __restrict__ Qg, const float* __restrict__ Kg,
         }
         float mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int key = kv0 + sub + 4 * i;
+        for (int i = 0; i < NS; ++i) {
+            const int key = kv0 + sub + TPR * i;
             if (key >= Lk || (CAUSAL && key > qrow + off)) s[i] = -INFINITY;
             mx = fmaxf(mx, s[i]);
         }
-        mx = group_max<4>(mx);
+        mx = group_max<TPR>(mx);
         const float m_new = fmaxf(m_run, mx * scale2);
         const float alpha = exp2_hw(m_run - m_new);
         m_run = m_new;
         float lsum = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < NS; ++i) {
             const float p = exp2_hw(__builtin_fmaf(s[i], scale2, -m_new));
             lsum += p;
-            Ps[r * PP + sub + 4 * i] = p;
+            Ps[r * PP + sub + TPR * i] = p;
         }
         l_run = l_run * alpha + lsum;
         __syncthreads();
 
 #pragma unroll
         for (int e = 0; e < NE; ++e) o[e] *= alpha;
+#pragma unroll 8
         for (int c = 0; c < BN; ++c) {
             const float p = Ps[r * PP + c];
 #pragma unroll
             for (int e = 0; e < NE; ++e) {
-                const f32x4_t vv = *(const f32x4_t*)(Vs + c * P + sub * 4 + e * 16);
+                const f32x4_t vv = *(const f32x4_t*)(Vs + c * P + sub * 4 + e * 4 * TPR);
                 o[e][0] = __builtin_fmaf(p, vv[0], o[e][0]);
                 o[e][1] = __builtin_fmaf(p, vv[1], o[e][1]);
                 o[e][2] = __builtin_fmaf(p, vv[2], o[e][2]);
@@ -139,12 +147,12 @@ void fwd_f32_kernel(const float* __restrict__ Qg, const float* __restrict__ Kg,
         }
     }
 
-    const float l_tot = group_sum<4>(l_run);
+    const float l_tot = group_sum<TPR>(l_run);
     if (qrow < Nq) {
         const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
         float* orow = Og + ((size_t)bh * Nq + qrow) * D;
 #pragma unroll
-        for (int e = 0; e < NE; ++e) *(f32x4_t*)(orow + sub * 4 + e * 16) = o[e] * inv;
+        for (int e = 0; e < NE; ++e) *(f32x4_t*)(orow + sub * 4 + e * 4 * TPR) = o[e] * inv;
         if (sub == 0 && LSEg)
             LSEg[(size_t)bh * Nq + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
     }

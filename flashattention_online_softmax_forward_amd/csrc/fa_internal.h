@@ -7,7 +7,7 @@
 namespace fa {
 
 constexpr int BM_FWD = 256;      // query rows per workgroup, bf16 forward (8 waves x 32)
-constexpr int BM_FWD_F32 = 64;   // query rows per workgroup, fp32 forward
+constexpr int BM_FWD_F32 = 16;   // query rows per workgroup, fp32 forward (16 threads per row)
 constexpr int BM_BWD = 128;      // rows (queries for dQ, keys for dK/dV) per workgroup, backward (4 waves x 32)
 
 // Causal alignment: none, top-left (key j visible from query i iff j <= i),
