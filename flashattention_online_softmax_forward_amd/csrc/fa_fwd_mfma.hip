@@ -48,9 +48,9 @@
 //   * Conditional rescaling (the FA4 refinement the iThome article describes
 //     after the alpha derivation): the running maximum of a wave's rows is
 //     only moved, and O and l rescaled, when some row's tile maximum exceeds it
-//     by more than 2^8 (base 2). Otherwise the tile is exponentiated against
-//     the stale maximum (P <= 256, safe in fp32 and bf16), which is exact once
-//     O is divided by the l accumulated on the same base.
+//     by more than 2^15 (base 2). Otherwise the tile is exponentiated against
+//     the stale maximum (P < 2^15, in range for fp16 and bf16 P and fp32 sums),
+//     which is exact once O is divided by the l accumulated on the same base.
 //   * Causal: key tiles past the block's last row are never visited, tiles a
 //     whole wave cannot see are skipped by that wave, masks are applied only on
 //     diagonal and ragged tiles, and the heaviest query blocks are issued first.
@@ -75,8 +75,13 @@ template <> struct Bf16Tile<64> { static constexpr int BN = 128; };
 
 constexpr int kFwdWaves = 8;
 constexpr int kFwdThreads = 64 * kFwdWaves;
-// Growth of a row maximum (log2 units) that forces a rescale of O and l.
-constexpr float kRescaleThreshold = 8.0f;
+// Growth of a row maximum (log2 units) that forces a rescale of O and l. A
+// row that keeps a stale maximum has every P below 2^15: within fp16's range
+// (largest finite 65504) as well as bf16's, and P is rounded relative to its
+// own magnitude, while l and O are fp32 sums, so no precision is lost. The
+// larger the threshold, the rarer the wave-wide rescale (rows whose maxima keep
+// growing, as with Q and K scaled by 3, took it on several tiles at 2^8).
+constexpr float kRescaleThreshold = 15.0f;
 
 // Key row (within a 32-key block) that lane-row i of the S^T A operand reads:
 // bits 2 and 3 swapped. With it, accumulator register r of lane (j, h) holds

@@ -136,14 +136,17 @@ def test_bf16_late_max_in_last_tile(fa):
 @pytest.mark.parametrize("causal", [False, True])
 def test_rescale_threshold_paths(fa, D, causal):
     """Row maxima that grow, tile after tile, by amounts just under, just over
-    and far over the 2^8 rescale threshold (base 2), then stop growing. Every
-    query row's scores are q . k_j = a_j with a single non-zero coordinate, so
-    the per-key base-2 score is a_j * scale * log2(e) exactly as designed."""
+    and far over the 2^15 rescale threshold (base 2), then stop growing: the
+    maximum kept after tile 0 is 0; 14.9 stays under it (P up to 2^14.9), 30.2
+    is 15.2 over (rescale), 45.0 is 14.8 over the new maximum (kept), 66 and
+    126 rescale, 126.5 and 132 stay. Every query row's scores are
+    q . k_j = a_j with a single non-zero coordinate, so the per-key base-2
+    score is a_j * scale * log2(e) exactly as designed."""
     N = 1024
     scale = 1.0 / math.sqrt(D)
     c2 = scale / math.log(2.0)                    # base-2 score per unit of a_j
     rng = np.random.default_rng(30)
-    steps = [0.0, 7.9, 15.8, 23.9, 44.0, 104.0, 104.5, 110.0]   # tile maxima (log2 units)
+    steps = [0.0, 14.9, 30.2, 45.0, 66.0, 126.0, 126.5, 132.0]   # tile maxima (log2 units)
     a = np.empty(N)
     tile = 64
     for t0 in range(0, N, tile):
