@@ -101,10 +101,13 @@ void decode_partial_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __re
             acc = group_sum<LPK>(acc);
             sc[u] = (base + u * G < j1) ? acc : -INFINITY;
         }
+        // NaN-propagating maxima: a NaN score must reach O and l even when a
+        // whole group's scores are NaN (fmaxf would keep m = -inf, and the
+        // group would then look empty to the merges below).
         float mx = sc[0];
 #pragma unroll
-        for (int u = 1; u < U; ++u) mx = fmaxf(mx, sc[u]);
-        const float m_new = fmaxf(m_run, mx);      // finite: key `base` is always live
+        for (int u = 1; u < U; ++u) mx = fmax_nan(mx, sc[u]);
+        const float m_new = fmax_nan(m_run, mx);   // not -inf: key `base` is always live
         const float alpha = exp2_hw(m_run - m_new);
         m_run = m_new;
         float p[U];
@@ -139,7 +142,7 @@ void decode_partial_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __re
     if (tid < D) {
         float M = -INFINITY;
 #pragma unroll 8
-        for (int gg = 0; gg < G; ++gg) M = fmaxf(M, sm_m[gg]);
+        for (int gg = 0; gg < G; ++gg) M = fmax_nan(M, sm_m[gg]);
         float L = 0.f, acc = 0.f;
         if (M != -INFINITY) {
 #pragma unroll 8
@@ -217,9 +220,11 @@ void decode_combine_kernel(const float* __restrict__ ws_o, const float* __restri
             lt += sm_l[g];
             ot += sm_o[g * D + tid];
         }
-        // No real key at all (every chunk empty): O = 0, LSE = -inf.
-        Og[(size_t)bh * D + tid] = (uint16_t)Elem<T>::pack2(lt > 0.f ? ot / lt : 0.f, 0.f);
-        if (tid == 0 && LSEg) LSEg[bh] = lt > 0.f ? (M + __log2f(lt)) * kLn2 : -INFINITY;
+        // No real key at all (every chunk empty): O = 0, LSE = -inf. A NaN
+        // (l = NaN, carried by a split whose m is NaN: its weight below is
+        // NaN) gives NaN in both.
+        Og[(size_t)bh * D + tid] = (uint16_t)Elem<T>::pack2(lt != 0.f ? ot / lt : 0.f, 0.f);
+        if (tid == 0 && LSEg) LSEg[bh] = lt != 0.f ? (M + __log2f(lt)) * kLn2 : -INFINITY;
     }
 }
 

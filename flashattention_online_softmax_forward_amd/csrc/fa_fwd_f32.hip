@@ -149,12 +149,13 @@ void fwd_f32_kernel(const float* __restrict__ Qg, const float* __restrict__ Kg,
 
     const float l_tot = group_sum<TPR>(l_run);
     if (qrow < Nq) {
-        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+        // l = 0: no key seen (O = 0, LSE = -inf); l = NaN: NaN in both.
+        const float inv = l_tot != 0.f ? 1.0f / l_tot : 0.f;
         float* orow = Og + ((size_t)bh * Nq + qrow) * D;
 #pragma unroll
         for (int e = 0; e < NE; ++e) *(f32x4_t*)(orow + sub * 4 + e * 4 * TPR) = o[e] * inv;
         if (sub == 0 && LSEg)
-            LSEg[(size_t)bh * Nq + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+            LSEg[(size_t)bh * Nq + qrow] = l_tot != 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
     }
 }
 

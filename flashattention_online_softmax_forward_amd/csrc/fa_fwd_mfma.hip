@@ -47,10 +47,14 @@
 //     masked out of S, and P = 0 meets a zero V row.
 //   * Conditional rescaling (the FA4 refinement the iThome article describes
 //     after the alpha derivation): the running maximum of a wave's rows is
-//     only moved, and O and l rescaled, when some row's tile maximum exceeds it
-//     by more than 2^15 (base 2). Otherwise the tile is exponentiated against
-//     the stale maximum (P < 2^15, in range for fp16 and bf16 P and fp32 sums),
-//     which is exact once O is divided by the l accumulated on the same base.
+//     only moved, and O and l rescaled, when a tile's P against it could
+//     exceed 2^15. Otherwise the tile is exponentiated against the stale
+//     maximum, which is exact once O is divided by the l accumulated on the
+//     same base. With D = 128, in waves whose first tile shows scores that
+//     do not stand far apart, later tiles are exponentiated first and the
+//     lanes' shares of the row sum are checked against the bound (the tile
+//     is redone when they exceed it); other waves, and D = 64, compare the
+//     tile maximum with the kept maximum plus the bound.
 //   * Causal: key tiles past the block's last row are never visited, tiles a
 //     whole wave cannot see are skipped by that wave, masks are applied only on
 //     diagonal and ragged tiles, and the heaviest query blocks are issued first.
@@ -75,13 +79,18 @@ template <> struct Bf16Tile<64> { static constexpr int BN = 128; };
 
 constexpr int kFwdWaves = 8;
 constexpr int kFwdThreads = 64 * kFwdWaves;
-// Growth of a row maximum (log2 units) that forces a rescale of O and l. A
-// row that keeps a stale maximum has every P below 2^15: within fp16's range
-// (largest finite 65504) as well as bf16's, and P is rounded relative to its
-// own magnitude, while l and O are fp32 sums, so no precision is lost. The
-// larger the threshold, the rarer the wave-wide rescale (rows whose maxima keep
-// growing, as with Q and K scaled by 3, took it on several tiles at 2^8).
+// Growth of a row maximum (log2 units) past which O and l are rescaled: a row
+// that keeps a stale maximum has every P at most 2^15, within fp16's range
+// (largest finite 65504) as well as bf16's (l and O are fp32 sums). bf16
+// could take larger P, but accuracy sets the bound there: right after the
+// maximum moves a row's largest P is exactly 1, under a stale maximum it is
+// rounded like any other, and in a row that one key dominates that rounding
+// reaches O almost unweighted. On causal 4x32x4096 inputs with Q and K scaled
+// by 3, bounds of 2^24 and 2^32 put sampled O errors past 2e-2.
 constexpr float kRescaleThreshold = 15.0f;
+// The same bound on a lane's share of a tile's row sum of P: at most 2^15
+// there means every P of the share is too (P >= 0).
+constexpr float kRescaleSum = 32768.0f;
 
 // Key row (within a 32-key block) that lane-row i of the S^T A operand reads:
 // bits 2 and 3 swapped. With it, accumulator register r of lane (j, h) holds
@@ -135,9 +144,13 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     constexpr bool kSplitLoads = D == 128;
     // Where the row maximum of a tile is taken (measured): with D = 64 the
     // MFMA step computes it, one maximum3 per PV MFMA after running QK(t)
-    // first, which takes VALU work off the heavier softmax step (+2-3%); with
-    // D = 128 the two steps are balanced and the softmax step keeps it.
+    // first, which takes VALU work off the heavier softmax step (+2-3%).
     constexpr bool kMaxInMfma = D == 64;
+    // With D = 128 the softmax step is bound by its VALU issue. Where the row
+    // maxima rarely move, it skips the row maximum: it exponentiates against
+    // the kept maximum and checks the row sums against the bound instead,
+    // taking the maximum only when they exceed it (see step_softmax).
+    constexpr bool kSumCheck = !kMaxInMfma;
 
     // Two K and two V tile buffers. Four distinct arrays, selected statically
     // (the phase loop below is unrolled over two tiles), let the compiler see
@@ -249,6 +262,9 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     // row's first visible key (finite, so masked scores give exp2(-inf) = 0).
     float m_run = kNoKeyMax;
     float l_run = 0.f;         // this lane's half of the running sum
+    // Whether later tiles are exponentiated before their maximum is known
+    // (wave-uniform; chosen on the first tile, see step_softmax).
+    bool spec = false;
 
     const int srow = s_row_perm(j);
     const int vb_blk = (lane >> 4) & 1;
@@ -418,12 +434,76 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
                     if ((r >> 3) * 16 + (r & 7) >= rel) s[c][r] = -INFINITY;
             }
         }
-        // Row maximum: from the MFMA step (kMaxInMfma) unless this tile was
-        // just masked.
-        const float m_tile = (!kMaxInMfma || ragged || diag) ? tile_max() : m_pre;
         // The row sum runs as several independent chains (one chain of
         // dependent adds would leave the VALU waiting on its own latency).
         constexpr int NCH = 4;
+        if constexpr (kSumCheck) {
+            // P of the tile against m_run, packed into the PV operands; returns
+            // this lane's share of the tile's row sum.
+            auto exp_tile = [&]() __attribute__((always_inline)) {
+                float lsc[NCH];    // chains start from the tile's first values (no 0 + p)
+#pragma unroll
+                for (int c = 0; c < NCB; ++c)
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        float p[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            p[e] = exp2_hw(__builtin_fmaf(s[c][u * 8 + e], scale2, -m_run));
+                            lsc[e % NCH] = (c == 0 && u == 0 && e < NCH) ? p[e] : lsc[e % NCH] + p[e];
+                        }
+                        u32x4_t w;
+                        w[0] = E::pack2(p[0], p[1]);
+                        w[1] = E::pack2(p[2], p[3]);
+                        w[2] = E::pack2(p[4], p[5]);
+                        w[3] = E::pack2(p[6], p[7]);
+                        pf[c * 2 + u] = __builtin_bit_cast(V8, w);
+                    }
+                return (lsc[0] + lsc[1]) + (lsc[2] + lsc[3]);
+            };
+            auto move_max = [&](float m_tile) __attribute__((always_inline)) {
+                const float m_new = fmaxf(m_run, m_tile);
+                const float alpha = exp2_hw(m_run - m_new);
+                m_run = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
+            };
+            float lsum;
+            if (spec) {
+                // Exponentiate against the kept maximum first. A lane whose
+                // share of the row sum is at most 2^15 has every P at most
+                // 2^15, so the tile stands as computed unless some lane of the
+                // wave went past that (or met a NaN, or overflowed); then the
+                // maximum moves (NaN-propagating tile maximum; fmaxf keeps
+                // m_run against a NaN, which then reaches O and l through P)
+                // and the tile is exponentiated again.
+                lsum = exp_tile();
+                if (__builtin_amdgcn_ballot_w64(!(lsum <= kRescaleSum))) {
+                    move_max(tile_max());
+                    lsum = exp_tile();
+                }
+            } else {
+                // The maximum first, moved only past the bound (always on the
+                // first tile, against kNoKeyMax; O and l are 0 there).
+                const float m_tile = tile_max();
+                if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleThreshold)) move_max(m_tile);
+                lsum = exp_tile();
+                // The first tile's row sums against their own maxima pick the
+                // wave's way for the later tiles: near 1 when one score stands
+                // far above the rest, as when the scores spread over tens of
+                // log2 units and the maximum keeps moving; near 10 for
+                // unit-variance Q and K, whose maxima settle after the first
+                // tile.
+                if (t == 0) spec = __builtin_popcountll(__builtin_amdgcn_ballot_w64(sum_xor32(lsum) < 3.0f)) <= 4;
+            }
+            l_run += lsum;
+        } else {
+        // Row maximum: from the MFMA step (kMaxInMfma) unless this tile was
+        // just masked.
+        const float m_tile = (!kMaxInMfma || ragged || diag) ? tile_max() : m_pre;
         // Move the maximum (and rescale O, l) only when some row of the wave
         // outgrew it by more than the threshold.
         if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleThreshold)) {
@@ -456,6 +536,7 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
             }
         const float lsum = (lsc[0] + lsc[1]) + (lsc[2] + lsc[3]);
         l_run += lsum;
+        }
     };
 
     // Ping-pong schedule. Every wave runs the same sequence of steps
@@ -570,9 +651,10 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     if (loader) __builtin_amdgcn_s_barrier();
 
     // Epilogue: O / l to bf16, LSE = (m + log2 l) * ln 2; a row that saw no
-    // key (l = 0, O = 0) gets O = 0 and LSE = -inf.
+    // key (l = 0, O = 0) gets O = 0 and LSE = -inf, and a row that met a NaN
+    // (l = NaN) gets NaN in both.
     const float l_tot = sum_xor32(l_run);
-    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    const float inv = l_tot != 0.f ? 1.0f / l_tot : 0.f;
     // O goes out through the wave's row staging (its Q reads ended before
     // the key loop) so that every store writes whole rows. O and LSE are
     // stored non-temporal: nothing here reads them again, and they would
@@ -608,7 +690,7 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
             if (wrow0 + it * RPI + lane / CPR < Nq) __builtin_nontemporal_store(w[it], (u32x4_t*)(orow + it * RPI * D));
     }
     if (qrow < Nq && h == 0 && LSEg)
-        __builtin_nontemporal_store(l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY, &LSEg[(size_t)bh * Nq + qrow]);
+        __builtin_nontemporal_store(l_tot != 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY, &LSEg[(size_t)bh * Nq + qrow]);
 }
 
 template <typename T, int D>

@@ -132,37 +132,62 @@ def test_bf16_late_max_in_last_tile(fa):
         check_bf16(f"late max causal={causal}", o, lse, ro, rl)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_rescale_threshold_paths(fa, D, causal):
-    """Row maxima that grow, tile after tile, by amounts just under, just over
-    and far over the 2^15 rescale threshold (base 2), then stop growing: the
-    maximum kept after tile 0 is 0; 14.9 stays under it (P up to 2^14.9), 30.2
-    is 15.2 over (rescale), 45.0 is 14.8 over the new maximum (kept), 66 and
-    126 rescale, 126.5 and 132 stay. Every query row's scores are
-    q . k_j = a_j with a single non-zero coordinate, so the per-key base-2
-    score is a_j * scale * log2(e) exactly as designed."""
+@pytest.mark.parametrize("peaky_first", [False, True])
+def test_rescale_threshold_paths(fa, dtype, D, causal, peaky_first):
+    """Row maxima that grow, tile after tile, by amounts under, just over and
+    far over the bound b = 15 on P (2^15, base 2), then stop growing. With
+    64-key tiles (D = 128) the maxima, in log2 units over the first tile's 0,
+    are b - 6.5 (kept: a lane's 32 P sum to at most 2^(b-1.5)), b + 0.7
+    (moved: one P alone is past 2^b), 2b - 6 (kept), 2b + 1.5 and 4b (moved),
+    4b + 1 (kept), 4b + 140 (moved; P against the kept maximum would
+    overflow fp32), then 4b + 139.5 (kept). With 128-key tiles (D = 64) the
+    same keys give maxima b - 6.5, 2b - 6 (moved, b + 0.5 up), 4b and
+    4b + 140 (moved), then only kept ones. The keys of a tile other than its
+    top lie 0.5 to 12 below it, except in the first tile when peaky_first:
+    20 to 30 below, so the first tile's row sums are ~1 and D = 128 waves
+    take the tile maximum before the exponentials on every later tile
+    (otherwise they exponentiate first and check the row sums). Every query
+    row is (1, 1, 0, ...) and key j holds a_j as the sum of its first two
+    coordinates (the input-type rounding of a_j and that of the remainder),
+    so the base-2 score of key j is a_j * scale * log2(e) to about 16 bits;
+    the margins above are checked on the scores the kernel sees (up to its
+    fp32 rounding)."""
     N = 1024
+    b = 15.0
     scale = 1.0 / math.sqrt(D)
     c2 = scale / math.log(2.0)                    # base-2 score per unit of a_j
     rng = np.random.default_rng(30)
-    steps = [0.0, 14.9, 30.2, 45.0, 66.0, 126.0, 126.5, 132.0]   # tile maxima (log2 units)
-    a = np.empty(N)
+    tops = [0.0, b - 6.5, b + 0.7, 2 * b - 6, 2 * b + 1.5, 4 * b, 4 * b + 1, 4 * b + 140, 4 * b + 139.5]
     tile = 64
+    a = np.empty(N)
+    top_idx = []
     for t0 in range(0, N, tile):
-        top = steps[min(t0 // tile, len(steps) - 1)]
-        a[t0:t0 + tile] = (top - rng.uniform(0.0, 12.0, tile)) / c2
-        a[t0 + int(rng.integers(0, tile))] = top / c2
-    q = torch.zeros(1, 2, N, D)
-    q[..., 0] = 1.0
-    k = torch.zeros(1, 2, N, D)
-    k[..., 0] = torch.from_numpy(a).float()
-    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
-    v = synth.normal((1, 2, N, D), torch.bfloat16, 31, synth.V_ID)
-    o, lse = fa.fa_forward(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal)
+        top = tops[min(t0 // tile, len(tops) - 1)]
+        lo, hi = (20.0, 30.0) if (peaky_first and t0 == 0) else (0.5, 12.0)
+        a[t0:t0 + tile] = (top - rng.uniform(lo, hi, tile)) / c2
+        top_idx.append(t0 + int(rng.integers(0, tile)))
+        a[top_idx[-1]] = top / c2
+    a_hi = torch.from_numpy(a).to(dtype)
+    a_lo = (torch.from_numpy(a) - a_hi.double()).to(dtype)
+    a = a_hi.double().numpy() + a_lo.double().numpy()        # the scores the kernel sees
+    got = [a[t0:t0 + tile].max() * c2 for t0 in range(0, N, tile)]
+    for t, top in enumerate(got):
+        want = tops[min(t, len(tops) - 1)]
+        assert abs(top - want) < 0.05 and a[top_idx[t]] * c2 == top, (t, top, want)
+    q = torch.zeros(1, 2, N, D, dtype=dtype)
+    q[..., :2] = 1.0
+    k = torch.zeros(1, 2, N, D, dtype=dtype)
+    k[..., 0] = a_hi
+    k[..., 1] = a_lo
+    v = synth.normal((1, 2, N, D), dtype, 31, synth.V_ID)
+    fwd = fa.fa_forward if dtype == torch.bfloat16 else fa.fa_forward_f16
+    o, lse = fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal)
     torch.cuda.synchronize()
     ro, rl = orc.attention(f64(q), f64(k), f64(v), scale, causal)
-    check_bf16(f"rescale paths D={D} causal={causal}", o, lse, ro, rl)
+    check_bf16(f"rescale paths {dtype} D={D} causal={causal}", o, lse, ro, rl)
 
 
 def test_huge_score_magnitudes(fa):
@@ -177,6 +202,51 @@ def test_huge_score_magnitudes(fa):
         print(f"[parity] huge scores causal={causal}: LSE rel max {err_l.max():.3e}", flush=True)
         assert np.isfinite(f64(o)).all() and err_l.max() <= 1e-5
         check_bf16(f"huge scores causal={causal}", o, lse, ro, f64(lse))
+
+
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 64), (torch.bfloat16, 128), (torch.float32, 64)])
+def test_nan_reaches_exactly_the_rows_that_see_it(fa, dtype, D):
+    """Causal, 700 keys. Head 1 has a NaN in key 300: every row that sees it
+    (300 and later) comes back with NaN in all of O and in its LSE, as the
+    softmax of a NaN score is NaN. Head 0 has a NaN in query row 50: that row
+    alone is NaN. Every other row, including rows that share a wave (and its
+    rescale vote) with rows that met a NaN, keeps the oracle's values."""
+    N, bad_k, bad_q = 700, 300, 50
+    q, k, v = synth.make_qkv(1, 2, N, N, D, dtype, seed=33)
+    k[0, 1, bad_k, 5] = float("nan")
+    q[0, 0, bad_q, 7] = float("nan")
+    fwd = fa.fa_forward if dtype == torch.bfloat16 else fa.fa_forward_f32
+    o, lse = fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True)
+    torch.cuda.synchronize()
+    o, lse = f64(o), f64(lse)
+    nan_rows = np.zeros((2, N), dtype=bool)
+    nan_rows[1, bad_k:] = True
+    nan_rows[0, bad_q] = True
+    ro, rl = orc.attention(f64(q), f64(k), f64(v), 1.0 / math.sqrt(D), True)
+    assert np.array_equal(np.isnan(rl[0]), nan_rows) and np.isnan(ro[0][nan_rows]).all()
+    assert np.isnan(o[0][nan_rows]).all() and np.isnan(lse[0][nan_rows]).all()
+    keep = ~nan_rows
+    assert not np.isnan(o[0][keep]).any() and not np.isnan(lse[0][keep]).any()
+    if dtype == torch.float32:
+        assert np.abs(o[0][keep] - ro[0][keep]).max() <= 1e-5 and np.abs(lse[0][keep] - rl[0][keep]).max() <= 1e-5
+    else:
+        check_bf16(f"NaN rows D={D} (the other rows)", o[0][keep], lse[0][keep], ro[0][keep], rl[0][keep])
+
+
+def test_nan_reaches_exactly_the_heads_that_see_it_decode(fa):
+    """Split-KV decode, 5000 keys in 8 splits: head 1 has a NaN in key 1234,
+    head 2 a NaN in its query (every score of that head is NaN, so whole
+    splits hold nothing but NaN scores): both heads come back NaN in O and
+    LSE; head 0 keeps the oracle's values."""
+    q, k, v = synth.make_qkv(1, 3, 1, 5000, 128, torch.bfloat16, seed=34)
+    k[0, 1, 1234, 3] = float("nan")
+    q[0, 2, 0, 9] = float("nan")
+    o, lse = fa.fa_decode_splitkv(q.to(DEV), k.to(DEV), v.to(DEV), num_splits=8)
+    torch.cuda.synchronize()
+    o, lse = f64(o), f64(lse)
+    assert np.isnan(o[0, 1:]).all() and np.isnan(lse[0, 1:]).all()
+    ro, rl = orc.attention(f64(q[:, :1]), f64(k[:, :1]), f64(v[:, :1]), 1.0 / math.sqrt(128), False)
+    check_bf16("decode NaN heads (the clean head)", o[:, :1], lse[:, :1], ro, rl)
 
 
 # ---------------------------------------------------------------- closed forms and invariants on the GPU
