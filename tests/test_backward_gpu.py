@@ -94,6 +94,12 @@ CASES = [
     (1, 4, 513, 513, 128, True, 3.0),      # scores std ~ 9 (the rescale-stress inputs)
     (1, 2, 1000, 1000, 64, True, 1.0),
     (2, 2, 129, 1025, 128, False, 3.0),
+    # Non-causal D = 128 (the ping-pong kernels, whose two wave groups take
+    # alternate 32-row query tiles): an odd tile count with a ragged second
+    # key block, two tiles the second of one row, two whole tiles.
+    (1, 2, 96, 160, 128, False, 1.0),
+    (1, 1, 33, 64, 128, False, 1.0),
+    (1, 1, 64, 64, 128, False, 3.0),
 ]
 
 
@@ -142,13 +148,14 @@ def test_backward_unseen_keys_are_zero(fa):
     check_case("bwd unseen keys", q, k, v, do, True, got)
 
 
-def test_backward_run_to_run_bitwise(fa):
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_run_to_run_bitwise(fa, causal):
     """No atomics: two calls give identical bits."""
     q, k, v = synth.make_qkv(1, 4, 700, 700, 128, torch.bfloat16, seed=25, device=DEV)
     do = synth.make_do(1, 4, 700, 128, torch.bfloat16, seed=25, device=DEV)
-    o, lse = fa.fa_forward(q, k, v, causal=True)
-    a = fa.fa_backward(q, k, v, o, do, lse, causal=True)
-    b = fa.fa_backward(q, k, v, o, do, lse, causal=True)
+    o, lse = fa.fa_forward(q, k, v, causal=causal)
+    a = fa.fa_backward(q, k, v, o, do, lse, causal=causal)
+    b = fa.fa_backward(q, k, v, o, do, lse, causal=causal)
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
@@ -167,15 +174,16 @@ def test_backward_rejects_bad_arguments(fa):
         fa.fa_backward(q, k, v, o, q, lse, dq=k)
 
 
-def test_backward_no_queries_zeroes_dk_dv(fa):
+@pytest.mark.parametrize("D,causal", [(64, True), (128, False)])
+def test_backward_no_queries_zeroes_dk_dv(fa, D, causal):
     """Nq = 0 < Nk: no query reads a key, so dK = dV = 0 (overwriting
     whatever the output buffers held)."""
-    k = synth.normal((1, 2, 70, 64), torch.bfloat16, 27, synth.K_ID, DEV)
-    v = synth.normal((1, 2, 70, 64), torch.bfloat16, 27, synth.V_ID, DEV)
-    q = torch.empty((1, 2, 0, 64), dtype=torch.bfloat16, device=DEV)
+    k = synth.normal((1, 2, 70, D), torch.bfloat16, 27, synth.K_ID, DEV)
+    v = synth.normal((1, 2, 70, D), torch.bfloat16, 27, synth.V_ID, DEV)
+    q = torch.empty((1, 2, 0, D), dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((1, 2, 0), dtype=torch.float32, device=DEV)
     dk = torch.ones_like(k)
     dv = torch.ones_like(v)
-    fa.fa_backward(q, k, v, q, q, lse, causal=True, dk=dk, dv=dv)
+    fa.fa_backward(q, k, v, q, q, lse, causal=causal, dk=dk, dv=dv)
     torch.cuda.synchronize()
     assert not dk.any() and not dv.any()
