@@ -210,6 +210,7 @@ BWD16_CASES = [
     (1, 2, 300, 300, 64, 1, None, 1.0),
     (2, 2, 129, 400, 128, 2, [400, 100], 1.0),
     (1, 2, 513, 513, 128, 1, None, 3.0),
+    (2, 2, 150, 333, 128, 0, [333, 90], 1.0),   # non-causal D = 128: ragged rows, padded keys
 ]
 
 
