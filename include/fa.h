@@ -45,10 +45,10 @@
  *     as the empty sums the definition reduces to: O = 0 and LSE = -inf, and
  *     its backward contributions are zero (the Pitfalls passage: such rows
  *     must not produce NaN).
- *   - NaN inputs: a row whose visible scores include a NaN (a NaN in its query
- *     row, or in a key or value row it attends) has a NaN softmax, so its O and
- *     LSE are NaN; rows that do not see the NaN are unaffected. Values in
- *     padding keys (past kv_lens[b]) are never read.
+ *   - NaN inputs: a NaN in a query row, or in a key row that row attends,
+ *     makes the row's softmax NaN, so its O and LSE are NaN; a NaN in a value
+ *     row it attends makes its O NaN. Rows that do not see the NaN are
+ *     unaffected. Padding keys (past kv_lens[b]) are never read.
  */
 #ifndef FA_MI355X_H
 #define FA_MI355X_H
