@@ -107,3 +107,33 @@ def test_decode_workload(fa):
     print(f"[parity] {w.name}: {len(pairs)} heads, O max {worst_o:.3e} mean {mean_o:.3e} LSE max {worst_l:.3e}",
           flush=True)
     assert worst_o <= BF16_MAX and mean_o <= BF16_MEAN and worst_l <= BF16_LSE
+
+
+@pytest.mark.parametrize("B,H,N,D,causal", [
+    (1, 1, 131072, 128, False),   # 2048 key tiles per workgroup, 512 query blocks
+    (64, 64, 256, 64, True),      # 4096 (batch, head) pairs of one query block each
+])
+def test_long_and_wide_shapes(fa, B, H, N, D, causal):
+    """Sizes past the workloads': a 131072-long sequence (a long key loop per
+    workgroup and row indices past 2^16) and a grid of 4096 heads. Sampled
+    rows (first, last, random) of a few (batch, head) pairs against the
+    oracle, each row over all of its keys."""
+    print(f"[case] long/wide {B}x{H}x{N}x{D} causal={causal}", flush=True)
+    q, k, v = synth.make_qkv(B, H, N, N, D, torch.bfloat16, seed=9, device=DEV)
+    scale = 1.0 / np.sqrt(D)
+    o, lse = fa.fa_forward(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(10)
+    pairs = {(0, 0), (B - 1, H - 1)} | {(int(rng.integers(0, B)), int(rng.integers(0, H))) for _ in range(3)}
+    rows = np.array(sorted(set(range(8)) | set(range(N - 8, N)) | set(rng.integers(0, N, 16).tolist())))
+    rows_t = torch.as_tensor(rows, device=DEV)
+    worst_o, worst_l = 0.0, 0.0
+    for b, h in sorted(pairs):
+        ro, rl = orc.attention_rows(f64(q[b, h].index_select(0, rows_t)), rows, f64(k[b, h]), f64(v[b, h]),
+                                    scale, causal)
+        eo = np.abs(f64(o[b, h].index_select(0, rows_t)) - ro)
+        el = np.abs(f64(lse[b, h].index_select(0, rows_t)) - rl)
+        assert np.isfinite(eo).all() and np.isfinite(el).all()
+        worst_o, worst_l = max(worst_o, eo.max()), max(worst_l, el.max())
+    print(f"[parity] long/wide {B}x{H}x{N}x{D}: O max {worst_o:.3e} LSE max {worst_l:.3e}", flush=True)
+    assert worst_o <= BF16_MAX and worst_l <= BF16_LSE
