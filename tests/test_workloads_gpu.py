@@ -137,3 +137,23 @@ def test_long_and_wide_shapes(fa, B, H, N, D, causal):
         worst_o, worst_l = max(worst_o, eo.max()), max(worst_l, el.max())
     print(f"[parity] long/wide {B}x{H}x{N}x{D}: O max {worst_o:.3e} LSE max {worst_l:.3e}", flush=True)
     assert worst_o <= BF16_MAX and worst_l <= BF16_LSE
+
+
+@pytest.mark.parametrize("Nk,S", [(1 << 20, 256), (100003, 1000)])
+def test_decode_long_cache_and_many_splits(fa, Nk, S):
+    """Decode past the workload's sizes: a cache of 2^20 keys in 256 splits of
+    4096, and a prime length in 1000 splits (chunks of 101 keys, the last ones
+    short or empty), against the oracle over every key of each head."""
+    B, H, D = 1, 2, 128
+    print(f"[case] decode Nk={Nk} splits={S}", flush=True)
+    q, k, v = synth.make_qkv(B, H, 1, Nk, D, torch.bfloat16, seed=11, device=DEV)
+    o, lse = fa.fa_decode_splitkv(q, k, v, num_splits=S)
+    torch.cuda.synchronize()
+    scale = 1.0 / np.sqrt(D)
+    worst_o, worst_l = 0.0, 0.0
+    for h in range(H):
+        ro, rl = orc.attention_rows(f64(q[0, h]), [0], f64(k[0, h]), f64(v[0, h]), scale, False)
+        worst_o = max(worst_o, float(np.abs(f64(o[0, h]) - ro).max()))
+        worst_l = max(worst_l, abs(float(lse[0, h]) - float(rl[0])))
+    print(f"[parity] decode Nk={Nk} splits={S}: O max {worst_o:.3e} LSE max {worst_l:.3e}", flush=True)
+    assert worst_o <= BF16_MAX and worst_l <= BF16_LSE
