@@ -46,9 +46,12 @@
  *     its backward contributions are zero (the Pitfalls passage: such rows
  *     must not produce NaN).
  *   - NaN inputs: a NaN in a query row, or in a key row that row attends,
- *     makes the row's softmax NaN, so its O and LSE are NaN; a NaN in a value
- *     row it attends makes its O NaN. Rows that do not see the NaN are
- *     unaffected. Padding keys (past kv_lens[b]) are never read.
+ *     makes the row's softmax NaN, so its O and LSE are NaN; no other row
+ *     changes. A NaN in column c of a value row makes column c of O NaN in
+ *     every row that attends it, and may also reach column c of a row that
+ *     masks that key causally but reads its key tile (the masked weight is
+ *     an exact zero, and 0 * NaN is NaN); the LSE and the other columns never
+ *     change. Padding keys (past kv_lens[b]) are never read.
  */
 #ifndef FA_MI355X_H
 #define FA_MI355X_H

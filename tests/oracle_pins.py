@@ -173,6 +173,39 @@ def pin_causal_edges(orc):
     assert not np.allclose(oc[:, :, 1:-1], of[:, :, 1:-1]), "causal mask had no effect"
 
 
+def pin_nan_stays_in_its_rows(orc):
+    """A NaN score reaches exactly the rows that attend it (the softmax of a
+    row holding a NaN score is NaN, O and LSE alike), and masked keys never
+    contribute: a NaN in a key that causal rows cannot see, or in a padding
+    key past kv_lens, leaves those rows as they were. A NaN in column c of a
+    value row makes column c of O NaN in the rows that attend it, and leaves
+    the LSE (a function of the scores alone) and the other columns as they
+    were. Where it lands in rows that mask it is not part of the promise: a
+    masked weight is an exact zero and 0 * NaN is NaN."""
+    q = _rand((1, 2, 9, 4), 40)
+    k = _rand((1, 2, 9, 4), 41)
+    v = _rand((1, 2, 9, 4), 42)
+    o0, l0 = orc.attention(q, k, v, 0.5, causal=True)
+    kn = k.copy()
+    kn[0, 1, 5, 2] = np.nan
+    o1, l1 = orc.attention(q, kn, v, 0.5, causal=True)
+    assert np.isnan(o1[0, 1, 5:]).all() and np.isnan(l1[0, 1, 5:]).all(), "rows that see the NaN key"
+    assert np.array_equal(o1[0, 1, :5], o0[0, 1, :5]) and np.array_equal(l1[0, 1, :5], l0[0, 1, :5]), \
+        "rows before the NaN key changed"
+    assert np.array_equal(o1[0, 0], o0[0, 0]) and np.array_equal(l1[0, 0], l0[0, 0]), "other head changed"
+    vn = v.copy()
+    vn[0, 0, 3, 1] = np.nan
+    o2, l2 = orc.attention(q, k, vn, 0.5, causal=True)
+    assert np.isnan(o2[0, 0, 3:, 1]).all() and np.array_equal(l2, l0), "NaN value row"
+    assert np.array_equal(np.delete(o2, 1, axis=-1), np.delete(o0, 1, axis=-1)), "other columns changed"
+    assert np.array_equal(o2[0, 1], o0[0, 1]), "other head changed"
+    kp = k.copy()
+    kp[0, :, 6:] = np.nan                  # padding: kv_lens = 6
+    o3, l3 = orc.attention(q, kp, v, 0.5, causal=False, kv_lens=[6])
+    o4, l4 = orc.attention(q, k, v, 0.5, causal=False, kv_lens=[6])
+    assert np.array_equal(o3, o4) and np.array_equal(l3, l4), "NaN padding keys leaked"
+
+
 # ---- an independent library routine -----------------------------------------
 
 def pin_torch_sdpa(orc):
@@ -592,4 +625,5 @@ ALL_PINS = [
     pin_backward_masks,
     pin_rope_closed_forms,
     pin_rope_relative_position,
+    pin_nan_stays_in_its_rows,
 ]
