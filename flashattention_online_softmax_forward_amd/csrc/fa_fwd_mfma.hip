@@ -191,10 +191,10 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
 
     // The wave's Q rows go to LDS with buffer loads (whole rows, four per
     // load; rows past Nq are out of the resource's range and arrive as zeros);
-    // they are read into registers after the first tile loads below.
+    // issued in the prologue below and read into registers from there.
     const int qwave = __builtin_amdgcn_readfirstlane(wave);
     uint16_t* const qst = row_lds + qwave * RB;
-    {
+    auto load_q = [&]() __attribute__((always_inline)) {
         constexpr int NQS = RB / 512;          // 1 KB slots per wave
         uint32_t qoff[NQS];
 #pragma unroll
@@ -215,7 +215,7 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
 #pragma unroll
         for (int g = 0; g < NQS; g += 4)
             buffer_lds_slots<4, 0, kCachePolicyNT>(rsrc, (LDS_AS void*)(LDS_AS uint16_t*)(qst + g * 512), qoff + g);
-    }
+    };
     // Q as the B operand: lane (j, h) holds row qrow, d = 16*kk + 8*h .. +7.
     u32x4_t qw[NKK];
     V8 qf[NKK];
@@ -592,12 +592,34 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    if (ntiles > 0) {
-        if (loader) dma(K, ld_koff, 0, k_lds0);
-        else if (kSplitLoads) dma(V, ld_voff, 0, v_lds0);
+    // Prologue. Group 0 needs its Q rows and K(0) for its first step, group 1
+    // its own Q rows a step later (and V(0) is read first by group 0's second
+    // step). With every workgroup of the launch reading its Q at once the
+    // loads queue at HBM, so group 0 issues first and starts as soon as its
+    // own loads have landed; group 1 issues after the first barrier and waits
+    // for its loads only after the second, while group 0's first step runs.
+    // Its extra barrier below (the one group 0 passes after that step) then
+    // publishes V(0).
+    if (loader) {
+        load_q();
+        if (ntiles > 0) dma(K, ld_koff, 0, k_lds0);
     }
-    __builtin_amdgcn_s_waitcnt(0xF70);
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (!loader) {
+        load_q();
+        if (kSplitLoads && ntiles > 0) dma(V, ld_voff, 0, v_lds0);
+    }
+    if (loader) __builtin_amdgcn_s_waitcnt(0xF70);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();              // K(0) complete
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xF70);         // group 1: its Q rows and V(0)
+    // The Q reads below must not move above the waits (the barrier and the
+    // wait intrinsics do not order memory accesses for the compiler).
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    __builtin_amdgcn_sched_barrier(0);
     // Q rows from the staging area into the B operand registers.
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
