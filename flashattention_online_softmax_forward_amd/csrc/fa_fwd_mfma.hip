@@ -58,6 +58,8 @@
 //   * Causal: key tiles past the block's last row are never visited, tiles a
 //     whole wave cannot see are skipped by that wave, masks are applied only on
 //     diagonal and ragged tiles, and the heaviest query blocks are issued first.
+//     With more query blocks than CUs the launch is persistent: one workgroup
+//     per CU works through a fixed list of blocks, paired heavy with light.
 //     Top-left alignment shows key j to query i iff j <= i; bottom-right iff
 //     j <= i + (Lk - Nq), one diagonal offset in every bound and mask.
 //   * Key padding: batch entry b has Lk = kv_lens[b] real keys (all Nk without
@@ -67,6 +69,8 @@
 //     -inf (the Pitfalls passage of the ML compiler page: exp2(-inf - -inf)
 //     would be NaN), so a masked score gives exp2(-inf) = 0 and a row that
 //     never sees a key ends with l = 0; it is written as O = 0, LSE = -inf.
+
+#include <atomic>
 
 #include "fa_device.h"
 #include "fa_internal.h"
@@ -120,7 +124,7 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
                      const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
                      float* __restrict__ LSEg, const int* __restrict__ kv_lens, int H, int Nq, int Nk,
                      int nqb, float scale2, int causal, const float* __restrict__ rope_cos,
-                     const float* __restrict__ rope_sin, int rope_style) {
+                     const float* __restrict__ rope_sin, int rope_style, int n_bh, int persist) {
     // The causal mode is a uniform run-time argument rather than a template
     // parameter: one code shape for all keeps register allocation stable.
     const bool CAUSAL = causal != kCausalNone;
@@ -166,563 +170,636 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     constexpr int RB = 32 * D;                 // elements of one wave's rows
     __shared__ __attribute__((aligned(1024))) uint16_t row_lds[kFwdWaves * RB];
 
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6;
-    const int group = wave >> 2;               // ping-pong group (one wave of each per SIMD)
-    const int lane = tid & 63;
-    const int j = lane & 31;
-    const int h = lane >> 5;
+    // Work of this workgroup: one query block or, in a persistent launch, a
+    // fixed list of them. Persistent launches serve causal masks with more
+    // query blocks than the grid: block qb of a head costs about qb + 1 key
+    // tiles, and handing such blocks to CUs one at a time in order leaves CUs
+    // idle (the dispatcher assigns workgroups to shader engines in turn and
+    // waits for a free CU in the next one's engine). Instead, the blocks of a
+    // head are paired (nqb - 1 - r with r), every pair costing the same; each
+    // XCD owns a contiguous range of pairs, so the heads in flight on it stay
+    // few and their K/V stays in its L2, and its workgroups take the pairs in
+    // turn, the heavy block of each first.
+    const int npair = (nqb + 1) / 2;
+    const int xcd = blockIdx.x & 7;            // workgroups go to the XCDs round-robin
+    const int per_xcd = gridDim.x >> 3;        // a persistent grid is a multiple of 8
+    const long long all_pairs = (long long)n_bh * npair;
+    const int p_lo = (int)(all_pairs * xcd / 8), p_hi = (int)(all_pairs * (xcd + 1) / 8);
+    for (int wi = 0;; ++wi) {
+        int bh, qb;
+        if (!persist) {
+            if (wi > 0) break;
+            const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
+            bh = logical / nqb;
+            qb = logical - bh * nqb;
+            if (CAUSAL) qb = nqb - 1 - qb;     // longest rows first
+        } else {
+            const int p = p_lo + (int)(blockIdx.x >> 3) + (wi >> 1) * per_xcd;
+            if (p >= p_hi) break;
+            bh = p / npair;
+            const int r = p - bh * npair;
+            qb = (wi & 1) ? r : nqb - 1 - r;
+            if ((wi & 1) && qb == nqb - 1 - r) continue;   // odd nqb: the middle block is alone
+        }
+        // The thread index is made opaque per block, so that the per-lane
+        // offsets and addresses derived from it are computed in each block
+        // rather than hoisted out of this loop and held in registers across
+        // every key loop.
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int wave = tid >> 6;
+        const int group = wave >> 2;           // ping-pong group (one wave of each per SIMD)
+        const int lane = tid & 63;
+        const int j = lane & 31;
+        const int h = lane >> 5;
 
-    const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
-    const int bh = logical / nqb;
-    int qb = logical - bh * nqb;
-    if (CAUSAL) qb = nqb - 1 - qb;             // longest rows first
-    const int q0 = qb * BM_FWD;
+        const int q0 = qb * BM_FWD;
 
-    const uint16_t* Q = Qg + (size_t)bh * Nq * D;
-    const uint16_t* K = Kg + (size_t)bh * Nk * D;
-    const uint16_t* V = Vg + (size_t)bh * Nk * D;
-    const int Lk = real_keys(kv_lens, bh / H, Nk);
-    // Causal diagonal offset: key j is visible from query i iff j <= i + off.
-    const int off = causal == kCausalBottomRight ? Lk - Nq : 0;
+        const uint16_t* Q = Qg + (size_t)bh * Nq * D;
+        const uint16_t* K = Kg + (size_t)bh * Nk * D;
+        const uint16_t* V = Vg + (size_t)bh * Nk * D;
+        const int Lk = real_keys(kv_lens, bh / H, Nk);
+        // Causal diagonal offset: key j is visible from query i iff j <= i + off.
+        const int off = causal == kCausalBottomRight ? Lk - Nq : 0;
 
-    const int wrow0 = q0 + wave * 32;
-    const int qrow = wrow0 + j;
+        const int wrow0 = q0 + wave * 32;
+        const int qrow = wrow0 + j;
 
-    // The wave's Q rows go to LDS with buffer loads (whole rows, four per
-    // load; rows past Nq are out of the resource's range and arrive as zeros);
-    // issued in the prologue below and read into registers from there.
-    const int qwave = __builtin_amdgcn_readfirstlane(wave);
-    uint16_t* const qst = row_lds + qwave * RB;
-    auto load_q = [&]() __attribute__((always_inline)) {
-        constexpr int NQS = RB / 512;          // 1 KB slots per wave
-        uint32_t qoff[NQS];
-#pragma unroll
-        for (int i = 0; i < NQS; ++i) {
-            const int p = i * 64 + lane;       // chunk of the wave's rows
+        // The wave's Q rows go to LDS with buffer loads (whole rows, four per
+        // load; rows past Nq are out of the resource's range and arrive as zeros);
+        // issued in the prologue below and read into registers from there.
+        const int qwave = __builtin_amdgcn_readfirstlane(wave);
+        uint16_t* const qst = row_lds + qwave * RB;
+        auto load_q = [&]() __attribute__((always_inline)) {
+            constexpr int NQS = RB / 512;          // 1 KB slots per wave
+            uint32_t qoff[NQS];
+    #pragma unroll
+            for (int i = 0; i < NQS; ++i) {
+                const int p = i * 64 + lane;       // chunk of the wave's rows
+                const int row = p / CPR;
+                qoff[i] = (uint32_t)(row * D + ((p % CPR) ^ (row & (CPR - 1))) * 8) * 2 - (i % 4) * 1024;
+            }
+            // From the wave-uniform index, so the resource is scalar (a per-lane
+            // resource would need a loop over its distinct values).
+            const int qrow0 = q0 + qwave * 32;
+            const int qrows = __builtin_amdgcn_readfirstlane(min(max(Nq - qrow0, 0), 32));
+            const int qfirst = __builtin_amdgcn_readfirstlane(min(qrow0, Nq));
+            const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(Q + (size_t)qfirst * D), (short)0, qrows * D * 2, kBufferRsrcWord3);
+            static_assert(NQS % 4 == 0, "slots in groups of 4");
+            // Each Q row is read by one workgroup only: streamed past L2.
+    #pragma unroll
+            for (int g = 0; g < NQS; g += 4)
+                buffer_lds_slots<4, 0, kCachePolicyNT>(rsrc, (LDS_AS void*)(LDS_AS uint16_t*)(qst + g * 512), qoff + g);
+        };
+        // Q as the B operand: lane (j, h) holds row qrow, d = 16*kk + 8*h .. +7.
+        u32x4_t qw[NKK];
+        V8 qf[NKK];
+
+        int kend = Lk;
+        if (CAUSAL) kend = max(0, min(Lk, min(q0 + BM_FWD, Nq) + off));
+        const int ntiles = (kend + BN - 1) / BN;
+        // Tiles this wave computes: a causal tile entirely after all its rows is skipped.
+        const int wlast = wrow0 + 31 + off;        // last key the wave's last row may see
+        const int my_tiles = CAUSAL ? (wlast < 0 ? 0 : min(ntiles, wlast / BN + 1)) : ntiles;
+
+        // Tile load slots: chunk p = (lwave*NLD + i)*64 + lane of a tile lands at
+        // byte 16*p of the LDS tile and holds logical chunk (p % CPR) ^ swz(row)
+        // of row p / CPR. The per-lane memory offsets are stored net of slot i's
+        // immediate offset (i KB).
+        const int lwave = __builtin_amdgcn_readfirstlane(wave & (kLoadWaves - 1));
+        uint32_t ld_koff[NLD], ld_voff[NLD];
+    #pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int p = (lwave * NLD + i) * 64 + lane;
             const int row = p / CPR;
-            qoff[i] = (uint32_t)(row * D + ((p % CPR) ^ (row & (CPR - 1))) * 8) * 2 - (i % 4) * 1024;
+            ld_koff[i] = (uint32_t)(row * D + ((p % CPR) ^ k_swz<CPR>(row)) * 8) * 2 - i * 1024;
+            ld_voff[i] = (uint32_t)(row * D + ((p % CPR) ^ v_swz<CPR>(row)) * 8) * 2 - i * 1024;
         }
-        // From the wave-uniform index, so the resource is scalar (a per-lane
-        // resource would need a loop over its distinct values).
-        const int qrow0 = q0 + qwave * 32;
-        const int qrows = __builtin_amdgcn_readfirstlane(min(max(Nq - qrow0, 0), 32));
-        const int qfirst = __builtin_amdgcn_readfirstlane(min(qrow0, Nq));
-        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(Q + (size_t)qfirst * D), (short)0, qrows * D * 2, kBufferRsrcWord3);
-        static_assert(NQS % 4 == 0, "slots in groups of 4");
-        // Each Q row is read by one workgroup only: streamed past L2.
-#pragma unroll
-        for (int g = 0; g < NQS; g += 4)
-            buffer_lds_slots<4, 0, kCachePolicyNT>(rsrc, (LDS_AS void*)(LDS_AS uint16_t*)(qst + g * 512), qoff + g);
-    };
-    // Q as the B operand: lane (j, h) holds row qrow, d = 16*kk + 8*h .. +7.
-    u32x4_t qw[NKK];
-    V8 qf[NKK];
+        // One tensor's tile at key kv0. The resource spans the tile's real keys
+        // only, so every address is a per-lane constant and only the resource base
+        // moves from tile to tile (scalar arithmetic).
+        auto dma = [&](const uint16_t* src, const uint32_t* voff, int kv0, uint16_t* dst) __attribute__((always_inline)) {
+            const int rows = min(Lk - kv0, BN);      // > 0: only tiles below kend <= Lk are loaded
+            const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(src + (size_t)kv0 * D), (short)0, rows * D * 2, kBufferRsrcWord3);
+            buffer_lds_slots<NLD>(rsrc, (LDS_AS void*)(LDS_AS uint16_t*)(dst + lwave * NLD * 512), voff);
+        };
 
-    int kend = Lk;
-    if (CAUSAL) kend = max(0, min(Lk, min(q0 + BM_FWD, Nq) + off));
-    const int ntiles = (kend + BN - 1) / BN;
-    // Tiles this wave computes: a causal tile entirely after all its rows is skipped.
-    const int wlast = wrow0 + 31 + off;        // last key the wave's last row may see
-    const int my_tiles = CAUSAL ? (wlast < 0 ? 0 : min(ntiles, wlast / BN + 1)) : ntiles;
+        f32x16_t acc_o[NDB];
+    #pragma unroll
+        for (int db = 0; db < NDB; ++db)
+    #pragma unroll
+            for (int r = 0; r < 16; ++r) acc_o[db][r] = 0.f;
+        f32x16_t s[NCB];            // S^T of the tile between its MFMA step and its softmax step
+        V8 pf[NPV];           // P of the tile between its softmax step and its PV step
 
-    // Tile load slots: chunk p = (lwave*NLD + i)*64 + lane of a tile lands at
-    // byte 16*p of the LDS tile and holds logical chunk (p % CPR) ^ swz(row)
-    // of row p / CPR. The per-lane memory offsets are stored net of slot i's
-    // immediate offset (i KB).
-    const int lwave = __builtin_amdgcn_readfirstlane(wave & (kLoadWaves - 1));
-    uint32_t ld_koff[NLD], ld_voff[NLD];
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-        const int p = (lwave * NLD + i) * 64 + lane;
-        const int row = p / CPR;
-        ld_koff[i] = (uint32_t)(row * D + ((p % CPR) ^ k_swz<CPR>(row)) * 8) * 2 - i * 1024;
-        ld_voff[i] = (uint32_t)(row * D + ((p % CPR) ^ v_swz<CPR>(row)) * 8) * 2 - i * 1024;
-    }
-    // One tensor's tile at key kv0. The resource spans the tile's real keys
-    // only, so every address is a per-lane constant and only the resource base
-    // moves from tile to tile (scalar arithmetic).
-    auto dma = [&](const uint16_t* src, const uint32_t* voff, int kv0, uint16_t* dst) __attribute__((always_inline)) {
-        const int rows = min(Lk - kv0, BN);      // > 0: only tiles below kend <= Lk are loaded
-        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(src + (size_t)kv0 * D), (short)0, rows * D * 2, kBufferRsrcWord3);
-        buffer_lds_slots<NLD>(rsrc, (LDS_AS void*)(LDS_AS uint16_t*)(dst + lwave * NLD * 512), voff);
-    };
+        // Base-2 scaled maximum the row is accumulated against; kNoKeyMax until the
+        // row's first visible key (finite, so masked scores give exp2(-inf) = 0).
+        float m_run = kNoKeyMax;
+        float l_run = 0.f;         // this lane's half of the running sum
+        // Whether later tiles are exponentiated before their maximum is known
+        // (wave-uniform; chosen on the first tile, see step_softmax).
+        bool spec = false;
 
-    f32x16_t acc_o[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_o[db][r] = 0.f;
-    f32x16_t s[NCB];            // S^T of the tile between its MFMA step and its softmax step
-    V8 pf[NPV];           // P of the tile between its softmax step and its PV step
+        const int srow = s_row_perm(j);
+        const int vb_blk = (lane >> 4) & 1;
+        const int v_s = lane & 15;
 
-    // Base-2 scaled maximum the row is accumulated against; kNoKeyMax until the
-    // row's first visible key (finite, so masked scores give exp2(-inf) = 0).
-    float m_run = kNoKeyMax;
-    float l_run = 0.f;         // this lane's half of the running sum
-    // Whether later tiles are exponentiated before their maximum is known
-    // (wave-uniform; chosen on the first tile, see step_softmax).
-    bool spec = false;
-
-    const int srow = s_row_perm(j);
-    const int vb_blk = (lane >> 4) & 1;
-    const int v_s = lane & 15;
-
-    // MFMA step of tile t: O^T += V^T P^T for tile t-1, then S^T = K Q^T for tile t.
-    // Only one wave per SIMD is in this step at a time, so it must keep the
-    // matrix core busy on its own: LDS operands are read a few MFMAs ahead, and
-    // sched_group_barrier pins that order (DS reads first, then one MFMA per
-    // group of reads).
-    constexpr int NPVM = NPV * NDB;            // PV MFMAs per tile
-    constexpr int NSM = NKK * NCB;             // QK MFMAs per tile
-    constexpr int LEAD = 4;                    // MFMAs of operand prefetch
-    auto pv_operand = [&](const uint16_t* vb_prev, int i) __attribute__((always_inline)) {
-        const int tt = i / NDB, db = i % NDB;
-        V4 part[2];
-#pragma unroll
-        for (int rd = 0; rd < 2; ++rd) {
-            const int key = tt * 16 + h * 8 + rd * 4 + (v_s >> 2);
-            const int col = db * 32 + vb_blk * 16 + (v_s & 3) * 4;
-            const int chunk = (col >> 3) ^ v_swz<CPR>(key);
-            const uint16_t* addr = vb_prev + key * D + chunk * 8 + (col & 7);
-            part[rd] = E::tr_read((LDS_AS V4*)(LDS_AS uint16_t*)addr);
-        }
-        return V8{part[0][0], part[0][1], part[0][2], part[0][3],
-                        part[1][0], part[1][1], part[1][2], part[1][3]};
-    };
-    auto qk_operand = [&](const uint16_t* kb, int i) __attribute__((always_inline)) {
-        const int kk = i / NCB, c = i % NCB;
-        const int row = c * 32 + srow;
-        return *(const V8*)(kb + row * D + (((kk * 2 + h) ^ k_swz<CPR>(row)) * 8));
-    };
-    // Scaled row maximum of tile t's scores (NaN-propagating).
-    auto tile_max = [&]() __attribute__((always_inline)) {
-        constexpr int NCH = 4;
-        float mxc[NCH];
-#pragma unroll
-        for (int k = 0; k < NCH; ++k) mxc[k] = s[0][k];
-#pragma unroll
-        for (int c = 0; c < NCB; ++c)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mxc[r % NCH] = fmax_nan(mxc[r % NCH], s[c][r]);
-        return max_xor32(fmax_nan(fmax_nan(mxc[0], mxc[1]), fmax_nan(mxc[2], mxc[3]))) * scale2;
-    };
-    float m_pre = kNoKeyMax;   // tile maximum taken by the MFMA step (kMaxInMfma)
-    auto step_mfma = [&](int t, const uint16_t* kb, const uint16_t* vb_prev) __attribute__((always_inline)) {
-        // lgkmcnt(0): nothing LDS-side is pending here (the barrier before
-        // this step drained it), but a scalar load of a kernel argument used
-        // only after the loop may be, on the first entry. Scalar loads return
-        // out of order, so while one may be pending the compiler can only
-        // wait for an operand with lgkmcnt(0), i.e. for every operand read
-        // issued ahead. Waiting here once lets the first MFMA of the step
-        // wait for its own operand alone.
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        __builtin_amdgcn_s_setprio(1);
-        const bool do_pv = t >= 1 && t - 1 < my_tiles;
-        const bool do_qk = t < my_tiles;
-        if (do_pv && do_qk && !kMaxInMfma) {
-            // PV(t-1) then QK(t) as one stream of 2*16 MFMAs, each operand read
-            // LEAD MFMAs ahead of its use.
-            constexpr int NM = NPVM + NSM;
-            auto operand = [&](int i) __attribute__((always_inline)) {
-                return i < NPVM ? pv_operand(vb_prev, i) : qk_operand(kb, i - NPVM);
-            };
-            const f32x16_t zero = {};
-            V8 ring[LEAD];
-#pragma unroll
-            for (int i = 0; i < LEAD; ++i) ring[i] = operand(i);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * LEAD, 0);
-#pragma unroll
-            for (int i = 0; i < NM; ++i) {
-                const V8 a = ring[i % LEAD];
-                if (i + LEAD < NM) ring[i % LEAD] = operand(i + LEAD);
-                if (i < NPVM)
-                    acc_o[i % NDB] = E::mfma(a, pf[i / NDB], acc_o[i % NDB]);
-                else  // the first d step of each key block starts from zero
-                    s[(i - NPVM) % NCB] = E::mfma(
-                        a, qf[(i - NPVM) / NCB], (i - NPVM) < NCB ? zero : s[(i - NPVM) % NCB]);
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                const int nx = i + LEAD;
-                if (nx < NPVM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                else if (nx < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        // MFMA step of tile t: O^T += V^T P^T for tile t-1, then S^T = K Q^T for tile t.
+        // Only one wave per SIMD is in this step at a time, so it must keep the
+        // matrix core busy on its own: LDS operands are read a few MFMAs ahead, and
+        // sched_group_barrier pins that order (DS reads first, then one MFMA per
+        // group of reads).
+        constexpr int NPVM = NPV * NDB;            // PV MFMAs per tile
+        constexpr int NSM = NKK * NCB;             // QK MFMAs per tile
+        constexpr int LEAD = 4;                    // MFMAs of operand prefetch
+        auto pv_operand = [&](const uint16_t* vb_prev, int i) __attribute__((always_inline)) {
+            const int tt = i / NDB, db = i % NDB;
+            V4 part[2];
+    #pragma unroll
+            for (int rd = 0; rd < 2; ++rd) {
+                const int key = tt * 16 + h * 8 + rd * 4 + (v_s >> 2);
+                const int col = db * 32 + vb_blk * 16 + (v_s & 3) * 4;
+                const int chunk = (col >> 3) ^ v_swz<CPR>(key);
+                const uint16_t* addr = vb_prev + key * D + chunk * 8 + (col & 7);
+                part[rd] = E::tr_read((LDS_AS V4*)(LDS_AS uint16_t*)addr);
             }
-        } else if (do_pv && do_qk) {
-            // QK(t) then PV(t-1); the row maximum of tile t runs on the VALU
-            // beside the PV MFMAs. The last 4 scores start 4 chains, the
-            // others join EPS per PV MFMA from the second one on (the QK
-            // results are complete by then).
-            constexpr int NM = NPVM + NSM;
-            auto operand = [&](int i) __attribute__((always_inline)) {
-                return i < NSM ? qk_operand(kb, i) : pv_operand(vb_prev, i - NSM);
-            };
-            const f32x16_t zero = {};
-            constexpr int NEL = NCB * 16;
-            constexpr int EPS = (NEL - 4 + NPVM - 2) / (NPVM - 1);
-            constexpr int NMX = (NEL - 4 + EPS - 1) / EPS;
-            static_assert(NMX <= NPVM - 1, "the maximum fits beside the PV MFMAs");
-            float mxc[4];
-            V8 ring[LEAD];
-#pragma unroll
-            for (int i = 0; i < LEAD; ++i) ring[i] = operand(i);
-            __builtin_amdgcn_sched_group_barrier(0x100, LEAD, 0);
-#pragma unroll
-            for (int i = 0; i < NM; ++i) {
-                const V8 a = ring[i % LEAD];
-                if (i + LEAD < NM) ring[i % LEAD] = operand(i + LEAD);
-                if (i < NSM)  // the first d step of each key block starts from zero
-                    s[i % NCB] = E::mfma(a, qf[i / NCB], i < NCB ? zero : s[i % NCB]);
-                else
-                    acc_o[(i - NSM) % NDB] = E::mfma(a, pf[(i - NSM) / NDB], acc_o[(i - NSM) % NDB]);
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                const int nx = i + LEAD;
-                if (nx < NSM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                else if (nx < NM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                // Empty asm statements pin each chain step to its iteration
-                // (pure arithmetic would otherwise float up to the end of the
-                // QK MFMAs); every step depends on its chain's previous pin.
-                const int k = i - NSM - 1;
-                if (k == -1) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        mxc[q] = s[(NEL - 4 + q) / 16][(NEL - 4 + q) % 16];
-                        asm volatile("" : "+v"(mxc[q]));
-                    }
+            return V8{part[0][0], part[0][1], part[0][2], part[0][3],
+                            part[1][0], part[1][1], part[1][2], part[1][3]};
+        };
+        auto qk_operand = [&](const uint16_t* kb, int i) __attribute__((always_inline)) {
+            const int kk = i / NCB, c = i % NCB;
+            const int row = c * 32 + srow;
+            return *(const V8*)(kb + row * D + (((kk * 2 + h) ^ k_swz<CPR>(row)) * 8));
+        };
+        // Scaled row maximum of tile t's scores (NaN-propagating).
+        auto tile_max = [&]() __attribute__((always_inline)) {
+            constexpr int NCH = 4;
+            float mxc[NCH];
+    #pragma unroll
+            for (int k = 0; k < NCH; ++k) mxc[k] = s[0][k];
+    #pragma unroll
+            for (int c = 0; c < NCB; ++c)
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) mxc[r % NCH] = fmax_nan(mxc[r % NCH], s[c][r]);
+            return max_xor32(fmax_nan(fmax_nan(mxc[0], mxc[1]), fmax_nan(mxc[2], mxc[3]))) * scale2;
+        };
+        float m_pre = kNoKeyMax;   // tile maximum taken by the MFMA step (kMaxInMfma)
+        auto step_mfma = [&](int t, const uint16_t* kb, const uint16_t* vb_prev) __attribute__((always_inline)) {
+            // lgkmcnt(0): nothing LDS-side is pending here (the barrier before
+            // this step drained it), but a scalar load of a kernel argument used
+            // only after the loop may be, on the first entry. Scalar loads return
+            // out of order, so while one may be pending the compiler can only
+            // wait for an operand with lgkmcnt(0), i.e. for every operand read
+            // issued ahead. Waiting here once lets the first MFMA of the step
+            // wait for its own operand alone.
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_s_setprio(1);
+            const bool do_pv = t >= 1 && t - 1 < my_tiles;
+            const bool do_qk = t < my_tiles;
+            if (do_pv && do_qk && !kMaxInMfma) {
+                // PV(t-1) then QK(t) as one stream of 2*16 MFMAs, each operand read
+                // LEAD MFMAs ahead of its use.
+                constexpr int NM = NPVM + NSM;
+                auto operand = [&](int i) __attribute__((always_inline)) {
+                    return i < NPVM ? pv_operand(vb_prev, i) : qk_operand(kb, i - NPVM);
+                };
+                const f32x16_t zero = {};
+                V8 ring[LEAD];
+    #pragma unroll
+                for (int i = 0; i < LEAD; ++i) ring[i] = operand(i);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * LEAD, 0);
+    #pragma unroll
+                for (int i = 0; i < NM; ++i) {
+                    const V8 a = ring[i % LEAD];
+                    if (i + LEAD < NM) ring[i % LEAD] = operand(i + LEAD);
+                    if (i < NPVM)
+                        acc_o[i % NDB] = E::mfma(a, pf[i / NDB], acc_o[i % NDB]);
+                    else  // the first d step of each key block starts from zero
+                        s[(i - NPVM) % NCB] = E::mfma(
+                            a, qf[(i - NPVM) / NCB], (i - NPVM) < NCB ? zero : s[(i - NPVM) % NCB]);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    const int nx = i + LEAD;
+                    if (nx < NPVM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    else if (nx < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 }
-                if (k >= 0 && k < NMX) {
-#pragma unroll
-                    for (int e = k * EPS; e < (k + 1) * EPS && e < NEL - 4; ++e)
-                        mxc[k % 4] = fmax_nan(mxc[k % 4], s[e / 16][e % 16]);
-                    asm volatile("" : "+v"(mxc[k % 4]));
-                }
-                if (i >= NSM) __builtin_amdgcn_sched_barrier(0);
-            }
-            m_pre = max_xor32(fmax_nan(fmax_nan(mxc[0], mxc[1]), fmax_nan(mxc[2], mxc[3]))) * scale2;
-        } else if (do_pv) {
-#pragma unroll
-            for (int i = 0; i < NPVM; ++i)
-                acc_o[i % NDB] = E::mfma(pv_operand(vb_prev, i), pf[i / NDB],
-                                                                         acc_o[i % NDB]);
-        } else if (do_qk) {
-            const f32x16_t zero = {};
-#pragma unroll
-            for (int i = 0; i < NSM; ++i)
-                s[i % NCB] = E::mfma(qk_operand(kb, i), qf[i / NCB],
-                                                                     i < NCB ? zero : s[i % NCB]);
-            if (kMaxInMfma) m_pre = tile_max();
-        }
-        __builtin_amdgcn_s_setprio(0);
-    };
-
-    // Softmax step of tile t: mask, row max, conditional rescale, P and its row sum.
-    auto step_softmax = [&](int t) __attribute__((always_inline)) {
-        if (t < 0 || t >= my_tiles) return;
-        const int kv0 = t * BN;
-        const bool ragged = kv0 + BN > Lk;
-        const bool diag = CAUSAL && (kv0 + BN - 1 > wrow0 + off);
-        if (ragged || diag) {
-#pragma unroll
-            for (int c = 0; c < NCB; ++c) {
-                // Keys from lim on are dead for this row: past Lk, or (causal)
-                // past qrow + off. Against the offset of key (c, r) within the
-                // lane's keys that is one compare with a small constant.
-                const int lim = CAUSAL ? min(Lk, qrow + off + 1) : Lk;
-                const int rel = lim - (kv0 + c * 32 + h * 8);
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if ((r >> 3) * 16 + (r & 7) >= rel) s[c][r] = -INFINITY;
-            }
-        }
-        // The row sum runs as several independent chains (one chain of
-        // dependent adds would leave the VALU waiting on its own latency).
-        constexpr int NCH = 4;
-        if constexpr (kSumCheck) {
-            // P of the tile against m_run, packed into the PV operands; returns
-            // this lane's share of the tile's row sum.
-            auto exp_tile = [&]() __attribute__((always_inline)) {
-                float lsc[NCH];    // chains start from the tile's first values (no 0 + p)
-#pragma unroll
-                for (int c = 0; c < NCB; ++c)
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        float p[8];
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            p[e] = exp2_hw(__builtin_fmaf(s[c][u * 8 + e], scale2, -m_run));
-                            lsc[e % NCH] = (c == 0 && u == 0 && e < NCH) ? p[e] : lsc[e % NCH] + p[e];
+            } else if (do_pv && do_qk) {
+                // QK(t) then PV(t-1); the row maximum of tile t runs on the VALU
+                // beside the PV MFMAs. The last 4 scores start 4 chains, the
+                // others join EPS per PV MFMA from the second one on (the QK
+                // results are complete by then).
+                constexpr int NM = NPVM + NSM;
+                auto operand = [&](int i) __attribute__((always_inline)) {
+                    return i < NSM ? qk_operand(kb, i) : pv_operand(vb_prev, i - NSM);
+                };
+                const f32x16_t zero = {};
+                constexpr int NEL = NCB * 16;
+                constexpr int EPS = (NEL - 4 + NPVM - 2) / (NPVM - 1);
+                constexpr int NMX = (NEL - 4 + EPS - 1) / EPS;
+                static_assert(NMX <= NPVM - 1, "the maximum fits beside the PV MFMAs");
+                float mxc[4];
+                V8 ring[LEAD];
+    #pragma unroll
+                for (int i = 0; i < LEAD; ++i) ring[i] = operand(i);
+                __builtin_amdgcn_sched_group_barrier(0x100, LEAD, 0);
+    #pragma unroll
+                for (int i = 0; i < NM; ++i) {
+                    const V8 a = ring[i % LEAD];
+                    if (i + LEAD < NM) ring[i % LEAD] = operand(i + LEAD);
+                    if (i < NSM)  // the first d step of each key block starts from zero
+                        s[i % NCB] = E::mfma(a, qf[i / NCB], i < NCB ? zero : s[i % NCB]);
+                    else
+                        acc_o[(i - NSM) % NDB] = E::mfma(a, pf[(i - NSM) / NDB], acc_o[(i - NSM) % NDB]);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    const int nx = i + LEAD;
+                    if (nx < NSM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    else if (nx < NM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    // Empty asm statements pin each chain step to its iteration
+                    // (pure arithmetic would otherwise float up to the end of the
+                    // QK MFMAs); every step depends on its chain's previous pin.
+                    const int k = i - NSM - 1;
+                    if (k == -1) {
+    #pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            mxc[q] = s[(NEL - 4 + q) / 16][(NEL - 4 + q) % 16];
+                            asm volatile("" : "+v"(mxc[q]));
                         }
-                        u32x4_t w;
-                        w[0] = E::pack2(p[0], p[1]);
-                        w[1] = E::pack2(p[2], p[3]);
-                        w[2] = E::pack2(p[4], p[5]);
-                        w[3] = E::pack2(p[6], p[7]);
-                        pf[c * 2 + u] = __builtin_bit_cast(V8, w);
                     }
-                return (lsc[0] + lsc[1]) + (lsc[2] + lsc[3]);
-            };
-            auto move_max = [&](float m_tile) __attribute__((always_inline)) {
+                    if (k >= 0 && k < NMX) {
+    #pragma unroll
+                        for (int e = k * EPS; e < (k + 1) * EPS && e < NEL - 4; ++e)
+                            mxc[k % 4] = fmax_nan(mxc[k % 4], s[e / 16][e % 16]);
+                        asm volatile("" : "+v"(mxc[k % 4]));
+                    }
+                    if (i >= NSM) __builtin_amdgcn_sched_barrier(0);
+                }
+                m_pre = max_xor32(fmax_nan(fmax_nan(mxc[0], mxc[1]), fmax_nan(mxc[2], mxc[3]))) * scale2;
+            } else if (do_pv) {
+    #pragma unroll
+                for (int i = 0; i < NPVM; ++i)
+                    acc_o[i % NDB] = E::mfma(pv_operand(vb_prev, i), pf[i / NDB],
+                                                                             acc_o[i % NDB]);
+            } else if (do_qk) {
+                const f32x16_t zero = {};
+    #pragma unroll
+                for (int i = 0; i < NSM; ++i)
+                    s[i % NCB] = E::mfma(qk_operand(kb, i), qf[i / NCB],
+                                                                         i < NCB ? zero : s[i % NCB]);
+                if (kMaxInMfma) m_pre = tile_max();
+            }
+            __builtin_amdgcn_s_setprio(0);
+        };
+
+        // Softmax step of tile t: mask, row max, conditional rescale, P and its row sum.
+        auto step_softmax = [&](int t) __attribute__((always_inline)) {
+            if (t < 0 || t >= my_tiles) return;
+            const int kv0 = t * BN;
+            const bool ragged = kv0 + BN > Lk;
+            const bool diag = CAUSAL && (kv0 + BN - 1 > wrow0 + off);
+            if (ragged || diag) {
+    #pragma unroll
+                for (int c = 0; c < NCB; ++c) {
+                    // Keys from lim on are dead for this row: past Lk, or (causal)
+                    // past qrow + off. Against the offset of key (c, r) within the
+                    // lane's keys that is one compare with a small constant.
+                    const int lim = CAUSAL ? min(Lk, qrow + off + 1) : Lk;
+                    const int rel = lim - (kv0 + c * 32 + h * 8);
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if ((r >> 3) * 16 + (r & 7) >= rel) s[c][r] = -INFINITY;
+                }
+            }
+            // The row sum runs as several independent chains (one chain of
+            // dependent adds would leave the VALU waiting on its own latency).
+            constexpr int NCH = 4;
+            if constexpr (kSumCheck) {
+                // P of the tile against m_run, packed into the PV operands; returns
+                // this lane's share of the tile's row sum.
+                auto exp_tile = [&]() __attribute__((always_inline)) {
+                    float lsc[NCH];    // chains start from the tile's first values (no 0 + p)
+    #pragma unroll
+                    for (int c = 0; c < NCB; ++c)
+    #pragma unroll
+                        for (int u = 0; u < 2; ++u) {
+                            float p[8];
+    #pragma unroll
+                            for (int e = 0; e < 8; ++e) {
+                                p[e] = exp2_hw(__builtin_fmaf(s[c][u * 8 + e], scale2, -m_run));
+                                lsc[e % NCH] = (c == 0 && u == 0 && e < NCH) ? p[e] : lsc[e % NCH] + p[e];
+                            }
+                            u32x4_t w;
+                            w[0] = E::pack2(p[0], p[1]);
+                            w[1] = E::pack2(p[2], p[3]);
+                            w[2] = E::pack2(p[4], p[5]);
+                            w[3] = E::pack2(p[6], p[7]);
+                            pf[c * 2 + u] = __builtin_bit_cast(V8, w);
+                        }
+                    return (lsc[0] + lsc[1]) + (lsc[2] + lsc[3]);
+                };
+                auto move_max = [&](float m_tile) __attribute__((always_inline)) {
+                    const float m_new = fmaxf(m_run, m_tile);
+                    const float alpha = exp2_hw(m_run - m_new);
+                    m_run = m_new;
+                    l_run *= alpha;
+    #pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+    #pragma unroll
+                        for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
+                };
+                float lsum;
+                if (spec) {
+                    // Exponentiate against the kept maximum first. A lane whose
+                    // share of the row sum is at most 2^15 has every P at most
+                    // 2^15, so the tile stands as computed unless some lane of the
+                    // wave went past that (or met a NaN, or overflowed); then the
+                    // maximum moves (NaN-propagating tile maximum; fmaxf keeps
+                    // m_run against a NaN, which then reaches O and l through P)
+                    // and the tile is exponentiated again.
+                    lsum = exp_tile();
+                    if (__builtin_amdgcn_ballot_w64(!(lsum <= kRescaleSum))) {
+                        move_max(tile_max());
+                        lsum = exp_tile();
+                    }
+                } else {
+                    // The maximum first, moved only past the bound (always on the
+                    // first tile, against kNoKeyMax; O and l are 0 there).
+                    const float m_tile = tile_max();
+                    if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleThreshold)) move_max(m_tile);
+                    lsum = exp_tile();
+                    // The first tile's row sums against their own maxima pick the
+                    // wave's way for the later tiles: near 1 when one score stands
+                    // far above the rest, as when the scores spread over tens of
+                    // log2 units and the maximum keeps moving; near 10 for
+                    // unit-variance Q and K, whose maxima settle after the first
+                    // tile.
+                    if (t == 0) spec = __builtin_popcountll(__builtin_amdgcn_ballot_w64(sum_xor32(lsum) < 3.0f)) <= 4;
+                }
+                l_run += lsum;
+            } else {
+            // Row maximum: from the MFMA step (kMaxInMfma) unless this tile was
+            // just masked.
+            const float m_tile = (!kMaxInMfma || ragged || diag) ? tile_max() : m_pre;
+            // Move the maximum (and rescale O, l) only when some row of the wave
+            // outgrew it by more than the threshold.
+            if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleThreshold)) {
                 const float m_new = fmaxf(m_run, m_tile);
                 const float alpha = exp2_hw(m_run - m_new);
                 m_run = m_new;
                 l_run *= alpha;
-#pragma unroll
+    #pragma unroll
                 for (int db = 0; db < NDB; ++db)
-#pragma unroll
+    #pragma unroll
                     for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
-            };
-            float lsum;
-            if (spec) {
-                // Exponentiate against the kept maximum first. A lane whose
-                // share of the row sum is at most 2^15 has every P at most
-                // 2^15, so the tile stands as computed unless some lane of the
-                // wave went past that (or met a NaN, or overflowed); then the
-                // maximum moves (NaN-propagating tile maximum; fmaxf keeps
-                // m_run against a NaN, which then reaches O and l through P)
-                // and the tile is exponentiated again.
-                lsum = exp_tile();
-                if (__builtin_amdgcn_ballot_w64(!(lsum <= kRescaleSum))) {
-                    move_max(tile_max());
-                    lsum = exp_tile();
-                }
-            } else {
-                // The maximum first, moved only past the bound (always on the
-                // first tile, against kNoKeyMax; O and l are 0 there).
-                const float m_tile = tile_max();
-                if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleThreshold)) move_max(m_tile);
-                lsum = exp_tile();
-                // The first tile's row sums against their own maxima pick the
-                // wave's way for the later tiles: near 1 when one score stands
-                // far above the rest, as when the scores spread over tens of
-                // log2 units and the maximum keeps moving; near 10 for
-                // unit-variance Q and K, whose maxima settle after the first
-                // tile.
-                if (t == 0) spec = __builtin_popcountll(__builtin_amdgcn_ballot_w64(sum_xor32(lsum) < 3.0f)) <= 4;
             }
+            float lsc[NCH];            // chains start from the tile's first values (no 0 + p)
+    #pragma unroll
+            for (int c = 0; c < NCB; ++c)
+    #pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    float p[8];
+    #pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        p[e] = exp2_hw(__builtin_fmaf(s[c][u * 8 + e], scale2, -m_run));
+                        lsc[e % NCH] = (c == 0 && u == 0 && e < NCH) ? p[e] : lsc[e % NCH] + p[e];
+                    }
+                    u32x4_t w;
+                    w[0] = E::pack2(p[0], p[1]);
+                    w[1] = E::pack2(p[2], p[3]);
+                    w[2] = E::pack2(p[4], p[5]);
+                    w[3] = E::pack2(p[6], p[7]);
+                    pf[c * 2 + u] = __builtin_bit_cast(V8, w);
+                }
+            const float lsum = (lsc[0] + lsc[1]) + (lsc[2] + lsc[3]);
             l_run += lsum;
-        } else {
-        // Row maximum: from the MFMA step (kMaxInMfma) unless this tile was
-        // just masked.
-        const float m_tile = (!kMaxInMfma || ragged || diag) ? tile_max() : m_pre;
-        // Move the maximum (and rescale O, l) only when some row of the wave
-        // outgrew it by more than the threshold.
-        if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleThreshold)) {
-            const float m_new = fmaxf(m_run, m_tile);
-            const float alpha = exp2_hw(m_run - m_new);
-            m_run = m_new;
-            l_run *= alpha;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
-        }
-        float lsc[NCH];            // chains start from the tile's first values (no 0 + p)
-#pragma unroll
-        for (int c = 0; c < NCB; ++c)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                float p[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    p[e] = exp2_hw(__builtin_fmaf(s[c][u * 8 + e], scale2, -m_run));
-                    lsc[e % NCH] = (c == 0 && u == 0 && e < NCH) ? p[e] : lsc[e % NCH] + p[e];
-                }
-                u32x4_t w;
-                w[0] = E::pack2(p[0], p[1]);
-                w[1] = E::pack2(p[2], p[3]);
-                w[2] = E::pack2(p[4], p[5]);
-                w[3] = E::pack2(p[6], p[7]);
-                pf[c * 2 + u] = __builtin_bit_cast(V8, w);
             }
-        const float lsum = (lsc[0] + lsc[1]) + (lsc[2] + lsc[3]);
-        l_run += lsum;
-        }
-    };
+        };
 
-    // Ping-pong schedule. Every wave runs the same sequence of steps
-    //     M(0) | S(0) | M(1) | S(1) | ... | M(T)
-    // separated by workgroup barriers, where M(t) = PV(t-1) + QK(t) on the
-    // matrix core and S(t) = softmax of tile t on the VALU. Group 1 executes
-    // one extra barrier first (and group 0 one at the end): barriers match by
-    // count, so group 1 always runs one step behind group 0 and, on every SIMD,
-    // one wave feeds the matrix core while the other does softmax.
-    // Tile buffers: K(t) in k_lds[t%2], V(t) in v_lds[t%2]. Every load is
-    // waited for at the end of the issuing wave's S step, and the barrier after
-    // it publishes the tile.
-    //   * Split loads (D = 128): group 0 loads K(t+1) during its S(t), which
-    //     runs beside group 1's M(t) (reading K(t), V(t-1)); the buffer's last
-    //     reader was group 1's M(t-1), and the first reader is group 0's
-    //     M(t+1). Group 1 loads V(t+1) during its S(t), which runs beside group
-    //     0's M(t+1) (reading K(t+1), V(t)); both groups last read the buffer
-    //     (as V(t-1)) in their M(t), and group 0's M(t+2) reads it first.
-    //     K(0) and V(0) are loaded before the loop.
-    //   * Group-0 loads (D = 64): group 0 loads K(t+1) and V(t) right after its
-    //     M(t); group 1's M(t-1), the last reader of both buffers, is over, and
-    //     group 0's M(t+1) is the first reader.
-    // Wave-uniform by construction; readfirstlane makes that visible, so the
-    // conditional barriers below are scalar branches.
-    const bool loader = __builtin_amdgcn_readfirstlane(group) == 0;
-    // One M step and one S step. The barrier between them protects no LDS data
-    // (it only keeps the two groups a step apart), so it is a plain s_barrier
-    // without the memory fence of __syncthreads, which would otherwise wait
-    // for the tile DMA still in flight. The barrier after the S step publishes
-    // the DMA that the loader waves have just waited for.
-    auto tile_steps = [&](int t, const uint16_t* kb, uint16_t* vb_prev, uint16_t* kb_next,
-                          uint16_t* vb_cur) __attribute__((always_inline)) {
-        step_mfma(t, kb, vb_prev);
-        if (!kSplitLoads && loader && t < ntiles) {
-            if (t + 1 < ntiles) dma(K, ld_koff, (t + 1) * BN, kb_next);
-            dma(V, ld_voff, t * BN, vb_cur);
+        // Ping-pong schedule. Every wave runs the same sequence of steps
+        //     M(0) | S(0) | M(1) | S(1) | ... | M(T)
+        // separated by workgroup barriers, where M(t) = PV(t-1) + QK(t) on the
+        // matrix core and S(t) = softmax of tile t on the VALU. Group 1 executes
+        // one extra barrier first (and group 0 one at the end): barriers match by
+        // count, so group 1 always runs one step behind group 0 and, on every SIMD,
+        // one wave feeds the matrix core while the other does softmax.
+        // Tile buffers: K(t) in k_lds[t%2], V(t) in v_lds[t%2]. Every load is
+        // waited for at the end of the issuing wave's S step, and the barrier after
+        // it publishes the tile.
+        //   * Split loads (D = 128): group 0 loads K(t+1) during its S(t), which
+        //     runs beside group 1's M(t) (reading K(t), V(t-1)); the buffer's last
+        //     reader was group 1's M(t-1), and the first reader is group 0's
+        //     M(t+1). Group 1 loads V(t+1) during its S(t), which runs beside group
+        //     0's M(t+1) (reading K(t+1), V(t)); both groups last read the buffer
+        //     (as V(t-1)) in their M(t), and group 0's M(t+2) reads it first.
+        //     K(0) and V(0) are loaded before the loop.
+        //   * Group-0 loads (D = 64): group 0 loads K(t+1) and V(t) right after its
+        //     M(t); group 1's M(t-1), the last reader of both buffers, is over, and
+        //     group 0's M(t+1) is the first reader.
+        // Wave-uniform by construction; readfirstlane makes that visible, so the
+        // conditional barriers below are scalar branches.
+        const bool loader = __builtin_amdgcn_readfirstlane(group) == 0;
+        // One M step and one S step. The barrier between them protects no LDS data
+        // (it only keeps the two groups a step apart), so it is a plain s_barrier
+        // without the memory fence of __syncthreads, which would otherwise wait
+        // for the tile DMA still in flight. The barrier after the S step publishes
+        // the DMA that the loader waves have just waited for.
+        auto tile_steps = [&](int t, const uint16_t* kb, uint16_t* vb_prev, uint16_t* kb_next,
+                              uint16_t* vb_cur) __attribute__((always_inline)) {
+            step_mfma(t, kb, vb_prev);
+            if (!kSplitLoads && loader && t < ntiles) {
+                if (t + 1 < ntiles) dma(K, ld_koff, (t + 1) * BN, kb_next);
+                dma(V, ld_voff, t * BN, vb_cur);
+            }
+            // sched_barrier(0): no instruction moves across the step boundary, so
+            // the two steps keep their own (smaller) sets of live registers.
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            if (kSplitLoads && t + 1 < ntiles) {
+                if (loader) dma(K, ld_koff, (t + 1) * BN, kb_next);
+                else dma(V, ld_voff, (t + 1) * BN, vb_prev);
+            }
+            step_softmax(t);
+            // vmcnt(0) on every wave (a no-op for waves with no DMA in flight), so
+            // the compiler knows no tile DMA is pending past this point.
+            __builtin_amdgcn_s_waitcnt(0xF70);
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+        };
+
+        // Prologue. Group 0 needs its Q rows and K(0) for its first step, group 1
+        // its own Q rows a step later (and V(0) is read first by group 0's second
+        // step). With every workgroup of the launch reading its Q at once the
+        // loads queue at HBM, so group 0 issues first and starts as soon as its
+        // own loads have landed; group 1 issues after the first barrier and waits
+        // for its loads only after the second, while group 0's first step runs.
+        // Its extra barrier below (the one group 0 passes after that step) then
+        // publishes V(0).
+        if (loader) {
+            load_q();
+            if (ntiles > 0) dma(K, ld_koff, 0, k_lds0);
         }
-        // sched_barrier(0): no instruction moves across the step boundary, so
-        // the two steps keep their own (smaller) sets of live registers.
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        if (kSplitLoads && t + 1 < ntiles) {
-            if (loader) dma(K, ld_koff, (t + 1) * BN, kb_next);
-            else dma(V, ld_voff, (t + 1) * BN, vb_prev);
+        if (!loader) {
+            load_q();
+            if (kSplitLoads && ntiles > 0) dma(V, ld_voff, 0, v_lds0);
         }
-        step_softmax(t);
-        // vmcnt(0) on every wave (a no-op for waves with no DMA in flight), so
-        // the compiler knows no tile DMA is pending past this point.
-        __builtin_amdgcn_s_waitcnt(0xF70);
+        if (loader) __builtin_amdgcn_s_waitcnt(0xF70);
         __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
+        __builtin_amdgcn_s_barrier();              // K(0) complete
         __builtin_amdgcn_sched_barrier(0);
-    };
-
-    // Prologue. Group 0 needs its Q rows and K(0) for its first step, group 1
-    // its own Q rows a step later (and V(0) is read first by group 0's second
-    // step). With every workgroup of the launch reading its Q at once the
-    // loads queue at HBM, so group 0 issues first and starts as soon as its
-    // own loads have landed; group 1 issues after the first barrier and waits
-    // for its loads only after the second, while group 0's first step runs.
-    // Its extra barrier below (the one group 0 passes after that step) then
-    // publishes V(0).
-    if (loader) {
-        load_q();
-        if (ntiles > 0) dma(K, ld_koff, 0, k_lds0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    if (!loader) {
-        load_q();
-        if (kSplitLoads && ntiles > 0) dma(V, ld_voff, 0, v_lds0);
-    }
-    if (loader) __builtin_amdgcn_s_waitcnt(0xF70);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();              // K(0) complete
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0xF70);         // group 1: its Q rows and V(0)
-    // The Q reads below must not move above the waits (the barrier and the
-    // wait intrinsics do not order memory accesses for the compiler).
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    __builtin_amdgcn_sched_barrier(0);
-    // Q rows from the staging area into the B operand registers.
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-        qw[kk] = *(LDS_AS const u32x4_t*)(LDS_AS const uint16_t*)(qst + j * D + ((kk * 2 + h) ^ (j & (CPR - 1))) * 8);
-    // Fused RoPE prologue on Q: the row is rotated in registers, once per
-    // workgroup, at its position (qrow, shifted by the bottom-right offset so
-    // the queries are the newest tokens). Both partners of every rotated pair
-    // are in this lane: d and d + D/2 (rotate-half) are chunks kk and
-    // kk + D/32 of the same half h; adjacent pairs share a chunk.
-    if (rope_cos && qrow < Nq) {
-        const int pos = max(0, qrow + off);
-        const float* cr = rope_cos + (size_t)pos * (D / 2);
-        const float* sr = rope_sin + (size_t)pos * (D / 2);
-        if (rope_style == kRopeHalf) {
-#pragma unroll
-            for (int kk = 0; kk < NKK / 2; ++kk) {
-                const int i0 = kk * 16 + h * 8;
-                const f32x4_t c0 = *(const f32x4_t*)(cr + i0), c1 = *(const f32x4_t*)(cr + i0 + 4);
-                const f32x4_t s0 = *(const f32x4_t*)(sr + i0), s1 = *(const f32x4_t*)(sr + i0 + 4);
-                const float c[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-                const float sn[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-                uint32_t a[4] = {qw[kk][0], qw[kk][1], qw[kk][2], qw[kk][3]};
-                uint32_t b[4] = {qw[kk + NKK / 2][0], qw[kk + NKK / 2][1], qw[kk + NKK / 2][2], qw[kk + NKK / 2][3]};
-                rope_half_chunks<T>(a, b, c, sn);
-                qw[kk] = u32x4_t{a[0], a[1], a[2], a[3]};
-                qw[kk + NKK / 2] = u32x4_t{b[0], b[1], b[2], b[3]};
-            }
-        } else {
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                const int p0 = kk * 8 + h * 4;
-                const f32x4_t c4 = *(const f32x4_t*)(cr + p0), s4 = *(const f32x4_t*)(sr + p0);
-                const float c[4] = {c4[0], c4[1], c4[2], c4[3]};
-                const float sn[4] = {s4[0], s4[1], s4[2], s4[3]};
-                uint32_t x[4] = {qw[kk][0], qw[kk][1], qw[kk][2], qw[kk][3]};
-                rope_pair_chunk<T>(x, c, sn);
-                qw[kk] = u32x4_t{x[0], x[1], x[2], x[3]};
+        __builtin_amdgcn_s_waitcnt(0xF70);         // group 1: its Q rows and V(0)
+        // The Q reads below must not move above the waits (the barrier and the
+        // wait intrinsics do not order memory accesses for the compiler).
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        __builtin_amdgcn_sched_barrier(0);
+        // Q rows from the staging area into the B operand registers.
+    #pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+            qw[kk] = *(LDS_AS const u32x4_t*)(LDS_AS const uint16_t*)(qst + j * D + ((kk * 2 + h) ^ (j & (CPR - 1))) * 8);
+        // Fused RoPE prologue on Q: the row is rotated in registers, once per
+        // workgroup, at its position (qrow, shifted by the bottom-right offset so
+        // the queries are the newest tokens). Both partners of every rotated pair
+        // are in this lane: d and d + D/2 (rotate-half) are chunks kk and
+        // kk + D/32 of the same half h; adjacent pairs share a chunk.
+        if (rope_cos && qrow < Nq) {
+            const int pos = max(0, qrow + off);
+            const float* cr = rope_cos + (size_t)pos * (D / 2);
+            const float* sr = rope_sin + (size_t)pos * (D / 2);
+            if (rope_style == kRopeHalf) {
+    #pragma unroll
+                for (int kk = 0; kk < NKK / 2; ++kk) {
+                    const int i0 = kk * 16 + h * 8;
+                    const f32x4_t c0 = *(const f32x4_t*)(cr + i0), c1 = *(const f32x4_t*)(cr + i0 + 4);
+                    const f32x4_t s0 = *(const f32x4_t*)(sr + i0), s1 = *(const f32x4_t*)(sr + i0 + 4);
+                    const float c[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+                    const float sn[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+                    uint32_t a[4] = {qw[kk][0], qw[kk][1], qw[kk][2], qw[kk][3]};
+                    uint32_t b[4] = {qw[kk + NKK / 2][0], qw[kk + NKK / 2][1], qw[kk + NKK / 2][2], qw[kk + NKK / 2][3]};
+                    rope_half_chunks<T>(a, b, c, sn);
+                    qw[kk] = u32x4_t{a[0], a[1], a[2], a[3]};
+                    qw[kk + NKK / 2] = u32x4_t{b[0], b[1], b[2], b[3]};
+                }
+            } else {
+    #pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) {
+                    const int p0 = kk * 8 + h * 4;
+                    const f32x4_t c4 = *(const f32x4_t*)(cr + p0), s4 = *(const f32x4_t*)(sr + p0);
+                    const float c[4] = {c4[0], c4[1], c4[2], c4[3]};
+                    const float sn[4] = {s4[0], s4[1], s4[2], s4[3]};
+                    uint32_t x[4] = {qw[kk][0], qw[kk][1], qw[kk][2], qw[kk][3]};
+                    rope_pair_chunk<T>(x, c, sn);
+                    qw[kk] = u32x4_t{x[0], x[1], x[2], x[3]};
+                }
             }
         }
-    }
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) qf[kk] = __builtin_bit_cast(V8, qw[kk]);
-    if (!loader) __builtin_amdgcn_s_barrier();
-    // Steps M(t), S(t) for t = 0 .. ntiles (M(ntiles) is the last PV product,
-    // S(ntiles) is empty); two tiles per iteration keep buffer choice static.
-    for (int t = 0; t <= ntiles; t += 2) {
-        tile_steps(t, k_lds0, v_lds1, k_lds1, v_lds0);
-        if (t + 1 > ntiles) break;
-        tile_steps(t + 1, k_lds1, v_lds0, k_lds0, v_lds1);
-    }
-    if (loader) __builtin_amdgcn_s_barrier();
-
-    // Epilogue: O / l to bf16, LSE = (m + log2 l) * ln 2; a row that saw no
-    // key (l = 0, O = 0) gets O = 0 and LSE = -inf, and a row that met a NaN
-    // (l = NaN) gets NaN in both.
-    const float l_tot = sum_xor32(l_run);
-    const float inv = l_tot != 0.f ? 1.0f / l_tot : 0.f;
-    // O goes out through the wave's row staging (its Q reads ended before
-    // the key loop) so that every store writes whole rows. O and LSE are
-    // stored non-temporal: nothing here reads them again, and they would
-    // otherwise take L2 lines that hold other workgroups' K/V tiles.
-    {
-        uint16_t* ost = qst;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4) {
-                const int c = db * 4 + a4;     // 16-byte chunk of the row: d = 8c .. 8c + 7
-                u32x2_t w;
-                w[0] = E::pack2(acc_o[db][a4 * 4 + 0] * inv, acc_o[db][a4 * 4 + 1] * inv);
-                w[1] = E::pack2(acc_o[db][a4 * 4 + 2] * inv, acc_o[db][a4 * 4 + 3] * inv);
-                *(LDS_AS u32x2_t*)(LDS_AS uint16_t*)(ost + j * D + (c ^ (j & (CPR - 1))) * 8 + h * 4) = w;
-            }
-        // The reads below take other lanes' writes: one wave's LDS
-        // operations complete in order once issued, and the fence keeps the
-        // compiler from moving the reads ahead.
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        constexpr int RPI = 64 / CPR;          // rows per read instruction
-        constexpr int NIT = 32 / RPI;
-        const int c = lane % CPR;
-        u32x4_t w[NIT];
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            const int r = it * RPI + lane / CPR;
-            w[it] = *(LDS_AS const u32x4_t*)(LDS_AS const uint16_t*)(ost + r * D + (c ^ (r & (CPR - 1))) * 8);
+    #pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) qf[kk] = __builtin_bit_cast(V8, qw[kk]);
+        if (!loader) __builtin_amdgcn_s_barrier();
+        // Steps M(t), S(t) for t = 0 .. ntiles (M(ntiles) is the last PV product,
+        // S(ntiles) is empty); two tiles per iteration keep buffer choice static.
+        for (int t = 0; t <= ntiles; t += 2) {
+            tile_steps(t, k_lds0, v_lds1, k_lds1, v_lds0);
+            if (t + 1 > ntiles) break;
+            tile_steps(t + 1, k_lds1, v_lds0, k_lds0, v_lds1);
         }
-        uint16_t* orow = Og + ((size_t)bh * Nq + wrow0 + lane / CPR) * D + c * 8;
-#pragma unroll
-        for (int it = 0; it < NIT; ++it)
-            if (wrow0 + it * RPI + lane / CPR < Nq) __builtin_nontemporal_store(w[it], (u32x4_t*)(orow + it * RPI * D));
+        if (loader) __builtin_amdgcn_s_barrier();
+
+        // Epilogue: O / l to bf16, LSE = (m + log2 l) * ln 2; a row that saw no
+        // key (l = 0, O = 0) gets O = 0 and LSE = -inf, and a row that met a NaN
+        // (l = NaN) gets NaN in both.
+        const float l_tot = sum_xor32(l_run);
+        const float inv = l_tot != 0.f ? 1.0f / l_tot : 0.f;
+        // O goes out through the wave's row staging (its Q reads ended before
+        // the key loop) so that every store writes whole rows. O and LSE are
+        // stored non-temporal: nothing here reads them again, and they would
+        // otherwise take L2 lines that hold other workgroups' K/V tiles.
+        {
+            uint16_t* ost = qst;
+    #pragma unroll
+            for (int db = 0; db < NDB; ++db)
+    #pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const int c = db * 4 + a4;     // 16-byte chunk of the row: d = 8c .. 8c + 7
+                    u32x2_t w;
+                    w[0] = E::pack2(acc_o[db][a4 * 4 + 0] * inv, acc_o[db][a4 * 4 + 1] * inv);
+                    w[1] = E::pack2(acc_o[db][a4 * 4 + 2] * inv, acc_o[db][a4 * 4 + 3] * inv);
+                    *(LDS_AS u32x2_t*)(LDS_AS uint16_t*)(ost + j * D + (c ^ (j & (CPR - 1))) * 8 + h * 4) = w;
+                }
+            // The reads below take other lanes' writes: one wave's LDS
+            // operations complete in order once issued, and the fence keeps the
+            // compiler from moving the reads ahead.
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            constexpr int RPI = 64 / CPR;          // rows per read instruction
+            constexpr int NIT = 32 / RPI;
+            const int c = lane % CPR;
+            u32x4_t w[NIT];
+    #pragma unroll
+            for (int it = 0; it < NIT; ++it) {
+                const int r = it * RPI + lane / CPR;
+                w[it] = *(LDS_AS const u32x4_t*)(LDS_AS const uint16_t*)(ost + r * D + (c ^ (r & (CPR - 1))) * 8);
+            }
+            uint16_t* orow = Og + ((size_t)bh * Nq + wrow0 + lane / CPR) * D + c * 8;
+    #pragma unroll
+            for (int it = 0; it < NIT; ++it)
+                if (wrow0 + it * RPI + lane / CPR < Nq) __builtin_nontemporal_store(w[it], (u32x4_t*)(orow + it * RPI * D));
+        }
+        if (qrow < Nq && h == 0 && LSEg)
+            __builtin_nontemporal_store(l_tot != 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY, &LSEg[(size_t)bh * Nq + qrow]);
+
+        // The next block's loads reuse the tile buffers and the row staging.
+        if (persist) __syncthreads();
     }
-    if (qrow < Nq && h == 0 && LSEg)
-        __builtin_nontemporal_store(l_tot != 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY, &LSEg[(size_t)bh * Nq + qrow]);
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];     // 0 until the device is first asked
+}  // namespace
+
+// Compute units of the current device, asked once per device.
+static hipError_t device_cu_count(int* n) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    int c = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
+        e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        g_cu_count[dev].store(c, std::memory_order_relaxed);
+    }
+    *n = c;
+    return hipSuccess;
 }
 
 template <typename T, int D>
 static hipError_t launch_one(const FwdArgs& a) {
     const int nqb = (a.Nq + BM_FWD - 1) / BM_FWD;
-    const int grid = a.B * a.H * nqb;
+    const int n_bh = a.B * a.H;
+    int grid = n_bh * nqb, persist = 0;
+    // Causal blocks of unequal cost and more of them than one per CU: a
+    // persistent grid of one workgroup per CU (the kernel fits one per CU)
+    // with the paired schedule above, when every workgroup gets a pair. Key
+    // padding makes the costs differ between batch entries as well, so it
+    // keeps the one-block-per-workgroup launch.
+    if (a.causal != kCausalNone && !a.kv_lens && grid > 0) {
+        int cus = 0;
+        const hipError_t e = device_cu_count(&cus);
+        if (e != hipSuccess) return e;
+        const int g = cus & ~7;
+        if (g > 0 && grid > g && (long long)n_bh * ((nqb + 1) / 2) >= g) {
+            grid = g;
+            persist = 1;
+        }
+    }
     hipLaunchKernelGGL((fwd_mfma_kernel<T, D>), dim3(grid), dim3(kFwdThreads), 0, a.stream,
                        (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
                        (uint16_t*)a.O, a.LSE, a.kv_lens, a.H, a.Nq, a.Nk, nqb, a.scale * kLog2e, a.causal,
-                       a.rope_cos, a.rope_sin, a.rope_style);
+                       a.rope_cos, a.rope_sin, a.rope_style, n_bh, persist);
     return hipGetLastError();
 }
 
