@@ -118,13 +118,13 @@ __device__ __forceinline__ int v_swz(int key) {
 
 #define LDS_AS __attribute__((address_space(3)))
 
-template <typename T, int D>
+template <typename T, int D, bool PERSIST>
 __global__ __launch_bounds__(kFwdThreads, 1)
 void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                      const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og,
                      float* __restrict__ LSEg, const int* __restrict__ kv_lens, int H, int Nq, int Nk,
                      int nqb, float scale2, int causal, const float* __restrict__ rope_cos,
-                     const float* __restrict__ rope_sin, int rope_style, int n_bh, int persist) {
+                     const float* __restrict__ rope_sin, int rope_style, int n_bh) {
     // The causal mode is a uniform run-time argument rather than a template
     // parameter: one code shape for all keeps register allocation stable.
     const bool CAUSAL = causal != kCausalNone;
@@ -187,7 +187,7 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     const int p_lo = (int)(all_pairs * xcd / 8), p_hi = (int)(all_pairs * (xcd + 1) / 8);
     for (int wi = 0;; ++wi) {
         int bh, qb;
-        if (!persist) {
+        if constexpr (!PERSIST) {
             if (wi > 0) break;
             const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
             bh = logical / nqb;
@@ -206,7 +206,7 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
         // rather than hoisted out of this loop and held in registers across
         // every key loop.
         int tid = threadIdx.x;
-        asm volatile("" : "+v"(tid));
+        if constexpr (PERSIST) asm volatile("" : "+v"(tid));
         const int wave = tid >> 6;
         const int group = wave >> 2;           // ping-pong group (one wave of each per SIMD)
         const int lane = tid & 63;
@@ -751,7 +751,7 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
             __builtin_nontemporal_store(l_tot != 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY, &LSEg[(size_t)bh * Nq + qrow]);
 
         // The next block's loads reuse the tile buffers and the row staging.
-        if (persist) __syncthreads();
+        if constexpr (PERSIST) __syncthreads();
     }
 }
 
@@ -760,8 +760,19 @@ constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];     // 0 until the device is first asked
 }  // namespace
 
-// Compute units of the current device, asked once per device.
-static hipError_t device_cu_count(int* n) {
+int paired_schedule_grid(int slots, int n_bh, int blocks_per_head) {
+    const int g = slots & ~7;
+    const long long blocks = (long long)n_bh * blocks_per_head;
+    const long long pairs = (long long)n_bh * ((blocks_per_head + 1) / 2);
+    if (g <= 0 || blocks <= g || pairs < g) return 0;
+    // The busiest workgroup runs ceil(pairs / g) pairs against pairs / g on
+    // average: keep that loss within 5% (a grid with 1.3 pairs per
+    // workgroup would run 2 on some and idle the rest half the time).
+    const long long rounds = (pairs + g - 1) / g;
+    return (rounds * g - pairs) * 20 <= pairs ? g : 0;
+}
+
+hipError_t device_cu_count(int* n) {
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
@@ -780,26 +791,30 @@ template <typename T, int D>
 static hipError_t launch_one(const FwdArgs& a) {
     const int nqb = (a.Nq + BM_FWD - 1) / BM_FWD;
     const int n_bh = a.B * a.H;
-    int grid = n_bh * nqb, persist = 0;
+    int grid = n_bh * nqb;
+    bool persist = false;
     // Causal blocks of unequal cost and more of them than one per CU: a
     // persistent grid of one workgroup per CU (the kernel fits one per CU)
-    // with the paired schedule above, when every workgroup gets a pair. Key
-    // padding makes the costs differ between batch entries as well, so it
-    // keeps the one-block-per-workgroup launch.
-    if (a.causal != kCausalNone && !a.kv_lens && grid > 0) {
+    // with the paired schedule above, when every workgroup gets a pair. Only
+    // for self-attention shapes (Nq = Nk, no key padding), where a block's
+    // cost is linear in its index and paired blocks cost the same; clamped
+    // costs (Nq != Nk) or padding that differs between batch entries keep the
+    // one-block-per-workgroup launch.
+    if (a.causal != kCausalNone && !a.kv_lens && a.Nq == a.Nk && grid > 0) {
         int cus = 0;
         const hipError_t e = device_cu_count(&cus);
         if (e != hipSuccess) return e;
-        const int g = cus & ~7;
-        if (g > 0 && grid > g && (long long)n_bh * ((nqb + 1) / 2) >= g) {
+        const int g = paired_schedule_grid(cus, n_bh, nqb);
+        if (g > 0) {
             grid = g;
-            persist = 1;
+            persist = true;
         }
     }
-    hipLaunchKernelGGL((fwd_mfma_kernel<T, D>), dim3(grid), dim3(kFwdThreads), 0, a.stream,
+    auto kern = persist ? fwd_mfma_kernel<T, D, true> : fwd_mfma_kernel<T, D, false>;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kFwdThreads), 0, a.stream,
                        (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
                        (uint16_t*)a.O, a.LSE, a.kv_lens, a.H, a.Nq, a.Nk, nqb, a.scale * kLog2e, a.causal,
-                       a.rope_cos, a.rope_sin, a.rope_style, n_bh, persist);
+                       a.rope_cos, a.rope_sin, a.rope_style, n_bh);
     return hipGetLastError();
 }
 

@@ -100,5 +100,12 @@ constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
 // device, then cached).
 hipError_t decode_scratch(void** ptr);
 hipError_t launch_bwd(const BwdArgs& a);
+// Compute units of the current device (asked once per device), for the
+// persistent causal launches.
+hipError_t device_cu_count(int* n);
+// Grid of a persistent launch with the paired causal schedule, given the
+// device's resident workgroup slots, or 0 when one block per workgroup is
+// the better launch (too few pairs, or pairs that do not share out evenly).
+int paired_schedule_grid(int slots, int n_bh, int blocks_per_head);
 
 }  // namespace fa
