@@ -335,7 +335,10 @@ def backward_leg(fa, synth, torch, w, steps, warmup):
     leg = {
         "workload": w.name, "ms_per_call": round(ms, 6), "value": round(tf, 3), "unit": "TFLOP/s",
         "algorithmic_flops": flops,
-        "roofline": roofline("bwd_dq_kernel + bwd_dkdv_kernel", "mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s",
+        # the two kernels of this shape: the ping-pong dQ kernel (non-causal,
+        # D = 128) or the 4-wave one, then dK/dV
+        "roofline": roofline(("bwd_dq_pp_kernel" if not w.causal and w.D == 128 else "bwd_dq_kernel")
+                             + " + bwd_dkdv_kernel", "mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s",
                              f"bwd_kernels_{w.name}", digest, True),
     }
     return leg, (q, k, v, do)
