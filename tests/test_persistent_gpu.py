@@ -112,3 +112,27 @@ def test_persistent_backward_matches_per_head(fa, case):
     torch.cuda.synchronize()
     got = (f64(o), f64(lse), f64(dq), f64(dk), f64(dv))
     check_case(f"persistent bwd {case}", q, k, v, do, causal, got, heads=[(0, 0), (B - 1, H - 1), (2, 5)])
+
+
+@pytest.mark.parametrize("kind", ["f16", "rope"])
+def test_persistent_forward_f16_and_rope(fa, kind):
+    """The fp16 forward and the fused-RoPE forward run the same persistent
+    kernel template: batched against head by head, bit for bit."""
+    B, H, N, D = 4, 32, 1024, 128
+    print(f"[case] persistent fwd {kind}", flush=True)
+    dtype = torch.float16 if kind == "f16" else torch.bfloat16
+    q, k, v = synth.make_qkv(B, H, N, N, D, dtype, seed=43)
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    if kind == "f16":
+        run = lambda a, b, c: fa.fa_forward_f16(a, b, c, causal=True)  # noqa: E731
+    else:
+        cos, sin = (t.to(DEV) for t in synth.rope_tables(N, D))
+        run = lambda a, b, c: fa.fa_forward_rope(a, b, c, cos, sin, causal=True)  # noqa: E731
+    o, lse = run(qd, kd, vd)
+    for b in range(B):
+        for h in range(H):
+            sl = lambda t: t[b:b + 1, h:h + 1].contiguous()  # noqa: E731
+            o1, l1 = run(sl(qd), sl(kd), sl(vd))
+            assert torch.equal(o[b, h], o1[0, 0]) and torch.equal(lse[b, h], l1[0, 0]), f"head ({b},{h})"
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all()
