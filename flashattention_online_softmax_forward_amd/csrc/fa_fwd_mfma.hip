@@ -58,8 +58,9 @@
 //   * Causal: key tiles past the block's last row are never visited, tiles a
 //     whole wave cannot see are skipped by that wave, masks are applied only on
 //     diagonal and ragged tiles, and the heaviest query blocks are issued first.
-//     With more query blocks than CUs the launch is persistent: one workgroup
-//     per CU works through a fixed list of blocks, paired heavy with light.
+//     Causal self-attention with more query blocks than CUs runs a persistent
+//     launch: one workgroup per CU works through a fixed list of blocks,
+//     paired heavy with light.
 //     Top-left alignment shows key j to query i iff j <= i; bottom-right iff
 //     j <= i + (Lk - Nq), one diagonal offset in every bound and mask.
 //   * Key padding: batch entry b has Lk = kv_lens[b] real keys (all Nk without
@@ -171,11 +172,11 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     __shared__ __attribute__((aligned(1024))) uint16_t row_lds[kFwdWaves * RB];
 
     // Work of this workgroup: one query block or, in a persistent launch, a
-    // fixed list of them. Persistent launches serve causal masks with more
-    // query blocks than the grid: block qb of a head costs about qb + 1 key
-    // tiles, and handing such blocks to CUs one at a time in order leaves CUs
-    // idle (the dispatcher assigns workgroups to shader engines in turn and
-    // waits for a free CU in the next one's engine). Instead, the blocks of a
+    // fixed list of them. Persistent launches serve causal self-attention
+    // with more query blocks than CUs: block qb of a head costs about qb + 1
+    // key tiles, and handing such blocks to CUs one at a time in order leaves
+    // CUs idle (the dispatcher assigns workgroups to shader engines in turn
+    // and waits for a free CU in the next one's engine). Instead, the blocks of a
     // head are paired (nqb - 1 - r with r), every pair costing the same; each
     // XCD owns a contiguous range of pairs, so the heads in flight on it stay
     // few and their K/V stays in its L2, and its workgroups take the pairs in
