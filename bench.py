@@ -75,7 +75,7 @@ LEGS = {
     "decode": ("decode_b16_h32_kv32768_d128_s64", "decode"),
     "backward": (HEADLINE, "backward"),
 }
-FWD_FILES = ["fa_fwd_mfma.hip", "fa_device.h", "fa_internal.h"]
+FWD_FILES = ["fa_fwd_mfma.hip", "fa_fwd_mfma16.hip", "fa_device.h", "fa_internal.h"]
 F32_FILES = ["fa_fwd_f32.hip", "fa_device.h", "fa_internal.h"]
 DEC_FILES = ["fa_decode.hip", "fa_device.h", "fa_internal.h"]
 BWD_FILES = ["fa_bwd.hip", "fa_device.h", "fa_internal.h"]
@@ -279,7 +279,9 @@ def forward_leg(fa, synth, torch, w, steps, warmup):
         kname, peak, files, dtype = "fwd_f32_kernel", PEAK_FP32_TFLOPS, F32_FILES, "f32"
     else:
         step = lambda: fa.fa_forward(q, k, v, causal=w.causal, scale=w.scale, out=out, lse=lse)  # noqa: E731
-        kname, peak, files, dtype = "fwd_mfma_kernel", PEAK_BF16_TFLOPS, FWD_FILES, "bf16"
+        # D = 128 runs the 16x16x32 kernel, D = 64 the 32x32x16 one
+        kname = "fwd_mfma16_kernel" if w.D == 128 else "fwd_mfma_kernel"
+        peak, files, dtype = PEAK_BF16_TFLOPS, FWD_FILES, "bf16"
     # The single-head fp32 kernel (~15 us) is shorter than one call's host
     # cost; its calls are queued ahead so the events time the kernels.
     ms = time_steps(step, steps, warmup, torch, queue_ahead=w.dtype == torch.float32)

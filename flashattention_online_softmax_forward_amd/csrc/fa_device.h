@@ -46,7 +46,7 @@ __device__ __forceinline__ float f16_hi(uint32_t w) {
 }
 
 // The 16-bit input types the MFMA kernels are instantiated for (bf16 and
-// fp16): operand vectors, the 32x32x16 MFMA with fp32 accumulation, the LDS
+// fp16): operand vectors, the 32x32x16 and 16x16x32 MFMAs with fp32 accumulation, the LDS
 // transpose read, round-to-nearest-even packing of two fp32 values, and
 // widening of the halves of a packed word.
 template <typename T> struct Elem;
@@ -55,6 +55,9 @@ template <> struct Elem<__bf16> {
     using v4 = bf16x4_t;
     __device__ static __forceinline__ f32x16_t mfma(v8 a, v8 b, f32x16_t c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ f32x4_t mfma16(v8 a, v8 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
     __device__ static __forceinline__ v4 tr_read(__attribute__((address_space(3))) v4* p) {
         return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p);
@@ -68,6 +71,9 @@ template <> struct Elem<_Float16> {
     using v4 = fp16x4_t;
     __device__ static __forceinline__ f32x16_t mfma(v8 a, v8 b, f32x16_t c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ f32x4_t mfma16(v8 a, v8 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
     }
     __device__ static __forceinline__ v4 tr_read(__attribute__((address_space(3))) v4* p) {
         return __builtin_amdgcn_ds_read_tr16_b64_v4f16(p);
@@ -153,6 +159,16 @@ __device__ __forceinline__ float max_xor32(float x) {
 }
 __device__ __forceinline__ float sum_xor32(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The same with lane (lane ^ 16), through v_permlane16_swap.
+__device__ __forceinline__ float max_xor16(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmax_nan(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 

@@ -1,7 +1,10 @@
-// FlashAttention forward for gfx950 with bf16 or fp16 inputs: MFMA for both
-// contractions (v_mfma_f32_32x32x16_bf16 / _f16, fp32 accumulation). The two
-// input types share every line below; Elem<T> supplies the MFMA, the LDS
-// transpose read and the round-to-nearest-even packing of P and O.
+// FlashAttention forward for gfx950 with D = 64 and bf16 or fp16 inputs: MFMA
+// for both contractions (v_mfma_f32_32x32x16_bf16 / _f16, fp32 accumulation).
+// The two input types share every line below; Elem<T> supplies the MFMA, the
+// LDS transpose read and the round-to-nearest-even packing of P and O. D = 128
+// runs fa_fwd_mfma16.hip, the same schedule on the 16x16x32 MFMA; the launch
+// helpers both use (the CU count, the persistent grid) are at the end of this
+// file.
 //
 // Method (iThome FlashAttention article, "three states"; ML compiler page,
 // section 11.9): a workgroup owns BM = 256 query rows of one (batch, head) and
@@ -50,11 +53,8 @@
 //     only moved, and O and l rescaled, when a tile's P against it could
 //     exceed 2^15. Otherwise the tile is exponentiated against the stale
 //     maximum, which is exact once O is divided by the l accumulated on the
-//     same base. With D = 128, in waves whose first tile shows scores that
-//     do not stand far apart, later tiles are exponentiated first and the
-//     lanes' shares of the row sum are checked against the bound (the tile
-//     is redone when they exceed it); other waves, and D = 64, compare the
-//     tile maximum with the kept maximum plus the bound.
+//     same base. The tile maximum, taken by the MFMA step, is compared with
+//     the kept maximum plus the bound.
 //   * Causal: key tiles past the block's last row are never visited, tiles a
 //     whole wave cannot see are skipped by that wave, masks are applied only on
 //     diagonal and ragged tiles, and the heaviest query blocks are issued first.
@@ -78,9 +78,6 @@
 
 namespace fa {
 
-template <int D> struct Bf16Tile;
-template <> struct Bf16Tile<128> { static constexpr int BN = 64; };
-template <> struct Bf16Tile<64> { static constexpr int BN = 128; };
 
 constexpr int kFwdWaves = 8;
 constexpr int kFwdThreads = 64 * kFwdWaves;
@@ -93,9 +90,6 @@ constexpr int kFwdThreads = 64 * kFwdWaves;
 // reaches O almost unweighted. On causal 4x32x4096 inputs with Q and K scaled
 // by 3, bounds of 2^24 and 2^32 put sampled O errors past 2e-2.
 constexpr float kRescaleThreshold = 15.0f;
-// The same bound on a lane's share of a tile's row sum of P: at most 2^15
-// there means every P of the share is too (P >= 0).
-constexpr float kRescaleSum = 32768.0f;
 
 // Key row (within a 32-key block) that lane-row i of the S^T A operand reads:
 // bits 2 and 3 swapped. With it, accumulator register r of lane (j, h) holds
@@ -104,18 +98,13 @@ __device__ __forceinline__ int s_row_perm(int i) {
     return (i & ~0xC) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
 
-// 16-byte chunk swizzles (CPR = chunks per row; LDS banks span 256 bytes).
+// 16-byte chunk swizzles of the 8-chunk (128-byte) rows; LDS banks span 256
+// bytes, two rows.
 // K: the 16 rows read together by one MFMA operand hit 16 distinct bank groups.
-template <int CPR>
-__device__ __forceinline__ int k_swz(int row) {
-    return CPR == 16 ? (row & 15) : ((row >> 1) & 7);
-}
+__device__ __forceinline__ int k_swz(int row) { return (row >> 1) & 7; }
 // V: the 4 keys x 4 column-quads of a transpose-read block, and the two blocks
 // that share a key range, hit distinct bank groups.
-template <int CPR>
-__device__ __forceinline__ int v_swz(int key) {
-    return CPR == 16 ? 4 * (key & 3) : 4 * ((key >> 1) & 1);
-}
+__device__ __forceinline__ int v_swz(int key) { return 4 * ((key >> 1) & 1); }
 
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -132,7 +121,8 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     using E = Elem<T>;
     using V8 = typename E::v8;
     using V4 = typename E::v4;
-    constexpr int BN = Bf16Tile<D>::BN;
+    static_assert(D == 64, "D = 128 runs fa_fwd_mfma16.hip");
+    constexpr int BN = 128;                    // keys per tile
     constexpr int TILE = BN * D;               // elements of one K (or V) tile
     constexpr int NCB = BN / 32;               // 32-key blocks of S^T
     constexpr int NKK = D / 16;                // 16-wide d steps of the S MFMA
@@ -142,20 +132,12 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
     constexpr int kLoadWaves = kFwdWaves / 2;     // one group's waves share a tile load
     constexpr int NLD = BN * CPR / (64 * kLoadWaves);   // DMA chunks per thread per tensor
     static_assert(NLD * 64 * kLoadWaves == BN * CPR, "loader covers the tile");
-    // Who loads tiles, and when (both measured): with D = 128, group 0 loads K
-    // and group 1 loads V, each at the start of its softmax step; with
-    // D = 64, whose softmax step has twice the exponentials per tile, group 0
-    // loads both right after its MFMA step.
-    constexpr bool kSplitLoads = D == 128;
-    // Where the row maximum of a tile is taken (measured): with D = 64 the
-    // MFMA step computes it, one maximum3 per PV MFMA after running QK(t)
-    // first, which takes VALU work off the heavier softmax step (+2-3%).
-    constexpr bool kMaxInMfma = D == 64;
-    // With D = 128 the softmax step is bound by its VALU issue. Where the row
-    // maxima rarely move, it skips the row maximum: it exponentiates against
-    // the kept maximum and checks the row sums against the bound instead,
-    // taking the maximum only when they exceed it (see step_softmax).
-    constexpr bool kSumCheck = !kMaxInMfma;
+    // Group 0 loads the tiles, both K(t+1) and V(t) right after its MFMA step:
+    // the softmax step, with its 64 exponentials per lane and tile, is the
+    // longer one (splitting the loads between the groups measured 2% slower).
+    // The MFMA step takes each tile's row maximum, one maximum3 per PV MFMA
+    // after running QK(t) first, which takes VALU work off the softmax step
+    // (+2-3%).
 
     // Two K and two V tile buffers. Four distinct arrays, selected statically
     // (the phase loop below is unrolled over two tiles), let the compiler see
@@ -274,8 +256,8 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
         for (int i = 0; i < NLD; ++i) {
             const int p = (lwave * NLD + i) * 64 + lane;
             const int row = p / CPR;
-            ld_koff[i] = (uint32_t)(row * D + ((p % CPR) ^ k_swz<CPR>(row)) * 8) * 2 - i * 1024;
-            ld_voff[i] = (uint32_t)(row * D + ((p % CPR) ^ v_swz<CPR>(row)) * 8) * 2 - i * 1024;
+            ld_koff[i] = (uint32_t)(row * D + ((p % CPR) ^ k_swz(row)) * 8) * 2 - i * 1024;
+            ld_voff[i] = (uint32_t)(row * D + ((p % CPR) ^ v_swz(row)) * 8) * 2 - i * 1024;
         }
         // One tensor's tile at key kv0. The resource spans the tile's real keys
         // only, so every address is a per-lane constant and only the resource base
@@ -299,9 +281,6 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
         // row's first visible key (finite, so masked scores give exp2(-inf) = 0).
         float m_run = kNoKeyMax;
         float l_run = 0.f;         // this lane's half of the running sum
-        // Whether later tiles are exponentiated before their maximum is known
-        // (wave-uniform; chosen on the first tile, see step_softmax).
-        bool spec = false;
 
         const int srow = s_row_perm(j);
         const int vb_blk = (lane >> 4) & 1;
@@ -322,7 +301,7 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
             for (int rd = 0; rd < 2; ++rd) {
                 const int key = tt * 16 + h * 8 + rd * 4 + (v_s >> 2);
                 const int col = db * 32 + vb_blk * 16 + (v_s & 3) * 4;
-                const int chunk = (col >> 3) ^ v_swz<CPR>(key);
+                const int chunk = (col >> 3) ^ v_swz(key);
                 const uint16_t* addr = vb_prev + key * D + chunk * 8 + (col & 7);
                 part[rd] = E::tr_read((LDS_AS V4*)(LDS_AS uint16_t*)addr);
             }
@@ -332,7 +311,7 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
         auto qk_operand = [&](const uint16_t* kb, int i) __attribute__((always_inline)) {
             const int kk = i / NCB, c = i % NCB;
             const int row = c * 32 + srow;
-            return *(const V8*)(kb + row * D + (((kk * 2 + h) ^ k_swz<CPR>(row)) * 8));
+            return *(const V8*)(kb + row * D + (((kk * 2 + h) ^ k_swz(row)) * 8));
         };
         // Scaled row maximum of tile t's scores (NaN-propagating).
         auto tile_max = [&]() __attribute__((always_inline)) {
@@ -346,7 +325,7 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
                 for (int r = 0; r < 16; ++r) mxc[r % NCH] = fmax_nan(mxc[r % NCH], s[c][r]);
             return max_xor32(fmax_nan(fmax_nan(mxc[0], mxc[1]), fmax_nan(mxc[2], mxc[3]))) * scale2;
         };
-        float m_pre = kNoKeyMax;   // tile maximum taken by the MFMA step (kMaxInMfma)
+        float m_pre = kNoKeyMax;   // tile maximum taken by the MFMA step
         auto step_mfma = [&](int t, const uint16_t* kb, const uint16_t* vb_prev) __attribute__((always_inline)) {
             // lgkmcnt(0): nothing LDS-side is pending here (the barrier before
             // this step drained it), but a scalar load of a kernel argument used
@@ -359,33 +338,7 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
             __builtin_amdgcn_s_setprio(1);
             const bool do_pv = t >= 1 && t - 1 < my_tiles;
             const bool do_qk = t < my_tiles;
-            if (do_pv && do_qk && !kMaxInMfma) {
-                // PV(t-1) then QK(t) as one stream of 2*16 MFMAs, each operand read
-                // LEAD MFMAs ahead of its use.
-                constexpr int NM = NPVM + NSM;
-                auto operand = [&](int i) __attribute__((always_inline)) {
-                    return i < NPVM ? pv_operand(vb_prev, i) : qk_operand(kb, i - NPVM);
-                };
-                const f32x16_t zero = {};
-                V8 ring[LEAD];
-    #pragma unroll
-                for (int i = 0; i < LEAD; ++i) ring[i] = operand(i);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2 * LEAD, 0);
-    #pragma unroll
-                for (int i = 0; i < NM; ++i) {
-                    const V8 a = ring[i % LEAD];
-                    if (i + LEAD < NM) ring[i % LEAD] = operand(i + LEAD);
-                    if (i < NPVM)
-                        acc_o[i % NDB] = E::mfma(a, pf[i / NDB], acc_o[i % NDB]);
-                    else  // the first d step of each key block starts from zero
-                        s[(i - NPVM) % NCB] = E::mfma(
-                            a, qf[(i - NPVM) / NCB], (i - NPVM) < NCB ? zero : s[(i - NPVM) % NCB]);
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    const int nx = i + LEAD;
-                    if (nx < NPVM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                    else if (nx < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
-            } else if (do_pv && do_qk) {
+            if (do_pv && do_qk) {
                 // QK(t) then PV(t-1); the row maximum of tile t runs on the VALU
                 // beside the PV MFMAs. The last 4 scores start 4 chains, the
                 // others join EPS per PV MFMA from the second one on (the QK
@@ -447,7 +400,7 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
                 for (int i = 0; i < NSM; ++i)
                     s[i % NCB] = E::mfma(qk_operand(kb, i), qf[i / NCB],
                                                                          i < NCB ? zero : s[i % NCB]);
-                if (kMaxInMfma) m_pre = tile_max();
+                m_pre = tile_max();
             }
             __builtin_amdgcn_s_setprio(0);
         };
@@ -474,73 +427,9 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
             // The row sum runs as several independent chains (one chain of
             // dependent adds would leave the VALU waiting on its own latency).
             constexpr int NCH = 4;
-            if constexpr (kSumCheck) {
-                // P of the tile against m_run, packed into the PV operands; returns
-                // this lane's share of the tile's row sum.
-                auto exp_tile = [&]() __attribute__((always_inline)) {
-                    float lsc[NCH];    // chains start from the tile's first values (no 0 + p)
-    #pragma unroll
-                    for (int c = 0; c < NCB; ++c)
-    #pragma unroll
-                        for (int u = 0; u < 2; ++u) {
-                            float p[8];
-    #pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                p[e] = exp2_hw(__builtin_fmaf(s[c][u * 8 + e], scale2, -m_run));
-                                lsc[e % NCH] = (c == 0 && u == 0 && e < NCH) ? p[e] : lsc[e % NCH] + p[e];
-                            }
-                            u32x4_t w;
-                            w[0] = E::pack2(p[0], p[1]);
-                            w[1] = E::pack2(p[2], p[3]);
-                            w[2] = E::pack2(p[4], p[5]);
-                            w[3] = E::pack2(p[6], p[7]);
-                            pf[c * 2 + u] = __builtin_bit_cast(V8, w);
-                        }
-                    return (lsc[0] + lsc[1]) + (lsc[2] + lsc[3]);
-                };
-                auto move_max = [&](float m_tile) __attribute__((always_inline)) {
-                    const float m_new = fmaxf(m_run, m_tile);
-                    const float alpha = exp2_hw(m_run - m_new);
-                    m_run = m_new;
-                    l_run *= alpha;
-    #pragma unroll
-                    for (int db = 0; db < NDB; ++db)
-    #pragma unroll
-                        for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
-                };
-                float lsum;
-                if (spec) {
-                    // Exponentiate against the kept maximum first. A lane whose
-                    // share of the row sum is at most 2^15 has every P at most
-                    // 2^15, so the tile stands as computed unless some lane of the
-                    // wave went past that (or met a NaN, or overflowed); then the
-                    // maximum moves (NaN-propagating tile maximum; fmaxf keeps
-                    // m_run against a NaN, which then reaches O and l through P)
-                    // and the tile is exponentiated again.
-                    lsum = exp_tile();
-                    if (__builtin_amdgcn_ballot_w64(!(lsum <= kRescaleSum))) {
-                        move_max(tile_max());
-                        lsum = exp_tile();
-                    }
-                } else {
-                    // The maximum first, moved only past the bound (always on the
-                    // first tile, against kNoKeyMax; O and l are 0 there).
-                    const float m_tile = tile_max();
-                    if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleThreshold)) move_max(m_tile);
-                    lsum = exp_tile();
-                    // The first tile's row sums against their own maxima pick the
-                    // wave's way for the later tiles: near 1 when one score stands
-                    // far above the rest, as when the scores spread over tens of
-                    // log2 units and the maximum keeps moving; near 10 for
-                    // unit-variance Q and K, whose maxima settle after the first
-                    // tile.
-                    if (t == 0) spec = __builtin_popcountll(__builtin_amdgcn_ballot_w64(sum_xor32(lsum) < 3.0f)) <= 4;
-                }
-                l_run += lsum;
-            } else {
-            // Row maximum: from the MFMA step (kMaxInMfma) unless this tile was
+            // Row maximum: from the MFMA step unless this tile was
             // just masked.
-            const float m_tile = (!kMaxInMfma || ragged || diag) ? tile_max() : m_pre;
+            const float m_tile = (ragged || diag) ? tile_max() : m_pre;
             // Move the maximum (and rescale O, l) only when some row of the wave
             // outgrew it by more than the threshold.
             if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleThreshold)) {
@@ -573,7 +462,6 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
                 }
             const float lsum = (lsc[0] + lsc[1]) + (lsc[2] + lsc[3]);
             l_run += lsum;
-            }
         };
 
         // Ping-pong schedule. Every wave runs the same sequence of steps
@@ -586,16 +474,9 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
         // Tile buffers: K(t) in k_lds[t%2], V(t) in v_lds[t%2]. Every load is
         // waited for at the end of the issuing wave's S step, and the barrier after
         // it publishes the tile.
-        //   * Split loads (D = 128): group 0 loads K(t+1) during its S(t), which
-        //     runs beside group 1's M(t) (reading K(t), V(t-1)); the buffer's last
-        //     reader was group 1's M(t-1), and the first reader is group 0's
-        //     M(t+1). Group 1 loads V(t+1) during its S(t), which runs beside group
-        //     0's M(t+1) (reading K(t+1), V(t)); both groups last read the buffer
-        //     (as V(t-1)) in their M(t), and group 0's M(t+2) reads it first.
-        //     K(0) and V(0) are loaded before the loop.
-        //   * Group-0 loads (D = 64): group 0 loads K(t+1) and V(t) right after its
-        //     M(t); group 1's M(t-1), the last reader of both buffers, is over, and
-        //     group 0's M(t+1) is the first reader.
+        // Group 0 loads K(t+1) and V(t) right after its M(t); group 1's M(t-1),
+        // the last reader of both buffers, is over, and group 0's M(t+1) is the
+        // first reader. K(0) is loaded before the loop.
         // Wave-uniform by construction; readfirstlane makes that visible, so the
         // conditional barriers below are scalar branches.
         const bool loader = __builtin_amdgcn_readfirstlane(group) == 0;
@@ -607,7 +488,7 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
         auto tile_steps = [&](int t, const uint16_t* kb, uint16_t* vb_prev, uint16_t* kb_next,
                               uint16_t* vb_cur) __attribute__((always_inline)) {
             step_mfma(t, kb, vb_prev);
-            if (!kSplitLoads && loader && t < ntiles) {
+            if (loader && t < ntiles) {
                 if (t + 1 < ntiles) dma(K, ld_koff, (t + 1) * BN, kb_next);
                 dma(V, ld_voff, t * BN, vb_cur);
             }
@@ -616,10 +497,6 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
             __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            if (kSplitLoads && t + 1 < ntiles) {
-                if (loader) dma(K, ld_koff, (t + 1) * BN, kb_next);
-                else dma(V, ld_voff, (t + 1) * BN, vb_prev);
-            }
             step_softmax(t);
             // vmcnt(0) on every wave (a no-op for waves with no DMA in flight), so
             // the compiler knows no tile DMA is pending past this point.
@@ -646,7 +523,6 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict
         __builtin_amdgcn_sched_barrier(0);
         if (!loader) {
             load_q();
-            if (kSplitLoads && ntiles > 0) dma(V, ld_voff, 0, v_lds0);
         }
         if (loader) __builtin_amdgcn_s_waitcnt(0xF70);
         __builtin_amdgcn_sched_barrier(0);
@@ -820,11 +696,11 @@ static hipError_t launch_one(const FwdArgs& a) {
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
-    return a.D == 128 ? launch_one<__bf16, 128>(a) : launch_one<__bf16, 64>(a);
+    return a.D == 128 ? launch_fwd16(a, false) : launch_one<__bf16, 64>(a);
 }
 
 hipError_t launch_fwd_f16(const FwdArgs& a) {
-    return a.D == 128 ? launch_one<_Float16, 128>(a) : launch_one<_Float16, 64>(a);
+    return a.D == 128 ? launch_fwd16(a, true) : launch_one<_Float16, 64>(a);
 }
 
 }  // namespace fa

@@ -90,6 +90,8 @@ struct BwdArgs {
 
 hipError_t launch_fwd_bf16(const FwdArgs& a);
 hipError_t launch_fwd_f16(const FwdArgs& a);
+// The D = 128 forward on the 16x16x32 MFMA (fa_fwd_mfma16.hip), bf16 or fp16.
+hipError_t launch_fwd16(const FwdArgs& a, bool f16);
 hipError_t launch_rope(const RopeArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
