@@ -994,7 +994,8 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
         if (e != hipSuccess) return e;
     }
     // With Nq = 0 the dK/dV kernel stages only V, runs no query tile and
-    // stores zeros.
+    // stores zeros. D = 128 runs on the 16x16x32 MFMA (fa_bwd16.hip).
+    if constexpr (D == 128) return launch_dkdv16(a, scale2, paired);
     const int nkb = (a.Nk + BM_BWD - 1) / BM_BWD;
     int grid = 0;
     if (paired) {

@@ -1,0 +1,482 @@
+// dK and dV of the backward pass with recompute for D = 128 on the 16x16x32
+// MFMA (v_mfma_f32_16x16x32_bf16 / _f16), the products of the "Backward with
+// recompute" exercise and section 11.9 of the ML compiler page that fall to
+// the key side:
+//     P = exp(scale Q K^T - L),  dP = dO V^T,  dS = P * (dP - D)
+//     dV = P^T dO,  dK = scale dS^T Q
+// (base-2 exponentials, L and scale multiplied by log2 e; D = rowsum(dO * O)
+// comes from the dQ kernel). It does what bwd_dkdv_kernel of fa_bwd.hip does
+// for D = 64 with the 32x32x16 MFMA, on the 16x16x32 shape: on random
+// operands that shape holds the chip's power limit at a higher engine clock
+// for the same work.
+//
+// 16x16x32 layouts (lane l, n = l % 16, g = l / 16): A lane holds row n,
+// k = 8g..8g+7; B lane holds k = 8g..8g+7 of column n; the accumulator lane
+// holds rows 4g..4g+3 of column n. A wave owns 32 keys (two column blocks kb2
+// of 16) and streams query tiles of 32 rows (two row blocks qb of 16):
+//   * S = Q K^T and dP = dO V^T: A = the tile's rows, B = K (registers) or V
+//     (the block's rows in LDS). Row m of block qb reads tile row
+//     8(m/4) + 4qb + m%4, so the lane ends with queries 8g + 4qb + 0..3 of its
+//     key: over both blocks, the eight queries 8g..8g+7 in order, which
+//     rounded to 16 bits is the B operand of the 32-query step of
+//     dV^T += dO^T P and dK^T += Q^T dS. P and dS never leave registers.
+//   * dO^T and Q^T (A of those products: row d = 16db + n, queries 8g..8g+7)
+//     are two ds_read_b64_tr_b16 of 4 rows each from the same tiles.
+//   * Tiles are staged once and read both ways: the 16-byte chunk swizzle
+//     2(row % 4) | 8(row bit 3) | (row bit 4) is free of bank conflicts for
+//     the row reads (16 lanes, 16 rows, one chunk) and the transpose reads (32
+//     lanes, 8 rows of 2 chunks), and ignores row bit 2, so the second row
+//     block and the second transpose read are constant offsets.
+
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+constexpr int kKvWaves = 4;
+constexpr int kKvThreads = 64 * kKvWaves;
+constexpr int kD = 128;
+constexpr int kCpr = kD / 8;                     // 16-byte chunks per row
+constexpr int kQT = 32;                          // query rows per streamed tile
+constexpr int kQTile = kQT * kD;
+constexpr int kNkc = kD / 32;                    // 32-wide d steps of S and dP
+constexpr int kNdb = kD / 16;                    // 16-wide d blocks of dK^T and dV^T
+static_assert(BM_BWD == 32 * kKvWaves, "32 keys per wave");
+
+#define LDS16B __attribute__((address_space(3)))
+
+// Chunk swizzle of the Q and dO tiles (see the header).
+__device__ __forceinline__ int tile_swz(int row) {
+    return ((row & 3) << 1) | (((row >> 3) & 1) << 3) | ((row >> 4) & 1);
+}
+// Chunk swizzle of the block's V rows, read by 16 consecutive rows at a time.
+__device__ __forceinline__ int vblk_swz(int row) { return row & 15; }
+
+// Staging of ROWS rows of a row-major [*, 128] array into LDS with chunk
+// swizzle SWZ: chunk p of the tile lands at byte 16p and holds logical chunk
+// (p % 16) ^ SWZ(row) of row p / 16. Wave w moves chunks (w*PER + i)*64 +
+// lane with buffer loads straight to LDS; rows past `valid` are outside the
+// resource and arrive as zeros.
+template <int ROWS, bool VBLK>
+struct Stage16 {
+    static constexpr int PER = ROWS * kCpr / kKvThreads;
+    static_assert(PER * kKvThreads == ROWS * kCpr, "whole chunks per lane");
+    static_assert(PER <= 4 || PER % 4 == 0, "slots in groups of up to 4");
+    uint32_t voff[PER];
+    __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int p = (wave * PER + i) * 64 + lane;
+            const int row = p / kCpr;
+            const int sw = VBLK ? vblk_swz(row) : tile_swz(row);
+            voff[i] = (uint32_t)(row * kD + ((p % kCpr) ^ sw) * 8) * 2u - (i % 4) * 1024u;
+        }
+    }
+    __device__ __forceinline__ void stage(const uint16_t* src, int valid, uint16_t* dst, int wave) const {
+        const __amdgpu_buffer_rsrc_t rsrc =
+            __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, valid * kD * 2, kBufferRsrcWord3);
+        if constexpr (PER <= 4) {
+            buffer_lds_slots<PER>(rsrc, (LDS16B void*)(LDS16B uint16_t*)(dst + wave * PER * 512), voff);
+        } else {
+#pragma unroll
+            for (int q = 0; q < PER; q += 4)
+                buffer_lds_slots<4>(rsrc, (LDS16B void*)(LDS16B uint16_t*)(dst + (wave * PER + q) * 512), voff + q);
+        }
+    }
+};
+
+// Store 32 rows x 128 of fp32 accumulators in the 16x16 layout (acc[db][kb2]:
+// lane (n, g) holds columns 16db + 4g .. +3 of row 16kb2 + n) as 16-bit
+// values times `mul` to rows dst[0 .. valid), through `stage` (32 x 128
+// elements of LDS private to the wave), so that every store writes whole
+// rows, 16 bytes per lane.
+template <typename T>
+__device__ __forceinline__ void store_rows16(uint16_t* dst, int valid, const f32x4_t (*acc)[2], float mul,
+                                             uint16_t* stage, int lane) {
+    const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const int row = kb2 * 16 + n;
+#pragma unroll
+        for (int db = 0; db < kNdb; ++db) {
+            const int c = 2 * db + (g >> 1);   // chunk of columns 16db + 4g .. +3
+            u32x2_t w;
+            w[0] = Elem<T>::pack2(acc[db][kb2][0] * mul, acc[db][kb2][1] * mul);
+            w[1] = Elem<T>::pack2(acc[db][kb2][2] * mul, acc[db][kb2][3] * mul);
+            *(LDS16B u32x2_t*)(LDS16B uint16_t*)(stage + row * kD + (c ^ (row & (kCpr - 1))) * 8 + (g & 1) * 4) = w;
+        }
+    }
+    // The reads take other lanes' writes: one wave's LDS operations complete
+    // in order once issued, and the fence keeps the compiler from moving the
+    // reads ahead.
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    constexpr int RPI = 64 / kCpr;             // rows per store instruction
+    constexpr int NIT = 32 / RPI;
+    const int c = lane % kCpr;
+    u32x4_t w[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int r = it * RPI + lane / kCpr;
+        w[it] = *(LDS16B const u32x4_t*)(LDS16B const uint16_t*)(stage + r * kD + (c ^ (r & (kCpr - 1))) * 8);
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int r = it * RPI + lane / kCpr;
+        if (r < valid) *(u32x4_t*)(dst + (size_t)r * kD + c * 8) = w[it];
+    }
+}
+
+// N steps step(i, op(i)), each operand read LEAD steps ahead and no further
+// (sched_barrier after every step), which bounds the registers a phase holds.
+template <int N, int LEAD, typename Op, typename Step>
+__device__ __forceinline__ void op_stream(Op op, Step step) {
+    decltype(op(0)) ring[LEAD];
+#pragma unroll
+    for (int i = 0; i < LEAD && i < N; ++i) ring[i] = op(i);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const auto a = ring[i % LEAD];
+        if (i + LEAD < N) ring[i % LEAD] = op(i + LEAD);
+        step(i, a);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+}  // namespace
+
+template <typename T, bool PERSIST>
+__global__ __launch_bounds__(kKvThreads, 2)
+void bwd_dkdv16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
+                       const uint16_t* __restrict__ Vg, const uint16_t* __restrict__ dOg,
+                       const float* __restrict__ LSEg, const float* __restrict__ Dg,
+                       uint16_t* __restrict__ dKg, uint16_t* __restrict__ dVg, const int* __restrict__ kv_lens,
+                       int H, int Nq, int Nk, int nkb, float scale, float scale2, int causal, int n_bh) {
+    using E = Elem<T>;
+    using V8 = typename E::v8;
+    using V4 = typename E::v4;
+    const bool CAUSAL = causal != kCausalNone;
+
+    // Small arrays first: every buffer's base then fits the 16-bit offset
+    // field of the LDS instructions.
+    __shared__ __attribute__((aligned(16))) float ld_lds[2][2 * kQT];  // per tile: L (base 2), then D
+    __shared__ __attribute__((aligned(1024))) uint16_t q_lds0[kQTile];
+    __shared__ __attribute__((aligned(1024))) uint16_t q_lds1[kQTile];
+    __shared__ __attribute__((aligned(1024))) uint16_t o_lds0[kQTile];   // dO tiles
+    __shared__ __attribute__((aligned(1024))) uint16_t o_lds1[kQTile];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_blk[BM_BWD * kD];
+
+    // One key block per workgroup or, in a persistent launch, the paired
+    // static schedule of bwd_dkdv_kernel (blocks r and nkb - 1 - r of a head
+    // at equal cost, contiguous pair ranges per XCD, taken in turn).
+    const int npair = (nkb + 1) / 2;
+    const int xcd = blockIdx.x & 7;
+    const int per_xcd = gridDim.x >> 3;
+    const long long all_pairs = (long long)n_bh * npair;
+    const int p_lo = (int)(all_pairs * xcd / 8), p_hi = (int)(all_pairs * (xcd + 1) / 8);
+    for (int wi = 0;; ++wi) {
+        int bh, kb;
+        if constexpr (!PERSIST) {
+            if (wi > 0) break;
+            const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
+            bh = logical / nkb;
+            kb = logical - bh * nkb;           // causal: low key blocks carry the most queries
+        } else {
+            const int p = p_lo + (int)(blockIdx.x >> 3) + (wi >> 1) * per_xcd;
+            if (p >= p_hi) break;
+            bh = p / npair;
+            const int r = p - bh * npair;
+            kb = (wi & 1) ? nkb - 1 - r : r;
+            if ((wi & 1) && nkb - 1 - r == r) continue;   // odd count: the middle block is alone
+        }
+        int tid = threadIdx.x;
+        if constexpr (PERSIST) asm volatile("" : "+v"(tid));
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int lane = tid & 63;
+        const int n = lane & 15;
+        const int g = lane >> 4;
+        const int k0 = kb * BM_BWD;
+        const int kw0 = k0 + wave * 32;
+        const int Lk = real_keys(kv_lens, bh / H, Nk);
+        const int doff = causal == kCausalBottomRight ? Lk - Nq : 0;   // key j visible from query i iff j <= i + doff
+
+        const uint16_t* Q = Qg + (size_t)bh * Nq * kD;
+        const uint16_t* dO = dOg + (size_t)bh * Nq * kD;
+        const float* L = LSEg + (size_t)bh * Nq;
+        const float* Dv = Dg + (size_t)bh * Nq;
+
+        // K of the wave's keys as B operands of S = Q K^T: key kw0 + 16kb2 + n,
+        // d = 32kc + 8g .. +7. Keys past Lk (padding) are zeros, so S = dP = 0
+        // there and, with P = 0, dS = 0 whatever the padded cache holds.
+        V8 kf[2][kNkc];
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+            const int key = kw0 + kb2 * 16 + n;
+#pragma unroll
+            for (int kc = 0; kc < kNkc; ++kc) {
+                u32x4_t w = {0u, 0u, 0u, 0u};
+                if (key < Lk) w = *(const u32x4_t*)(Kg + ((size_t)bh * Nk + key) * kD + kc * 32 + g * 8);
+                kf[kb2][kc] = __builtin_bit_cast(V8, w);
+            }
+        }
+        // Lane byte offsets of the LDS operand reads, the same for every tile
+        // buffer (whose base folds into the instruction's offset field):
+        //   rowoff[kc]: tile row 8(n/4) + n%4, chunk 4kc + g (row block 1: +4 rows);
+        //   troff[db]: tile row 8g + n/4, columns 16db + 4(n%4) .. +3 (second
+        //              transpose read: +4 rows);
+        //   voff[kc]: V block row 32 wave + n, chunk 4kc + g (kb2 = 1: +16 rows).
+        uint32_t rowoff[kNkc], troff[kNdb], voff[kNkc];
+        {
+            const int r = 8 * (n >> 2) + (n & 3);
+            const int q = 8 * g + (n >> 2);
+            const int vr = wave * 32 + n;
+#pragma unroll
+            for (int kc = 0; kc < kNkc; ++kc) {
+                rowoff[kc] = (uint32_t)(r * kD + ((4 * kc + g) ^ tile_swz(r)) * 8) * 2u;
+                voff[kc] = (uint32_t)(vr * kD + ((4 * kc + g) ^ vblk_swz(vr)) * 8) * 2u;
+                asm volatile("" : "+v"(rowoff[kc]));
+                asm volatile("" : "+v"(voff[kc]));
+            }
+#pragma unroll
+            for (int db = 0; db < kNdb; ++db) {
+                const int col = 16 * db + 4 * (n & 3);
+                troff[db] = (uint32_t)(q * kD + ((col >> 3) ^ tile_swz(q)) * 8 + (col & 7)) * 2u;
+                asm volatile("" : "+v"(troff[db]));
+            }
+        }
+        auto a_row = [&](const uint16_t* tile, int qb, int kc) __attribute__((always_inline)) {
+            return *(LDS16B const V8*)((LDS16B const char*)(LDS16B const uint16_t*)tile + rowoff[kc] + qb * 1024);
+        };
+        auto a_tr = [&](const uint16_t* tile, int db) __attribute__((always_inline)) {
+            const V4 p0 = E::tr_read((LDS16B V4*)((LDS16B char*)(LDS16B uint16_t*)tile + troff[db]));
+            const V4 p1 = E::tr_read((LDS16B V4*)((LDS16B char*)(LDS16B uint16_t*)tile + troff[db] + 1024));
+            return V8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+        };
+        auto b_v = [&](int kb2, int kc) __attribute__((always_inline)) {
+            return *(LDS16B const V8*)((LDS16B const char*)(LDS16B const uint16_t*)v_blk + voff[kc] + kb2 * 16 * kD * 2);
+        };
+
+        // dK^T and dV^T: acc[db][kb2], lane (n, g) holds d = 16db + 4g .. +3 of key 16kb2 + n.
+        f32x4_t adk[kNdb][2], adv[kNdb][2];
+#pragma unroll
+        for (int db = 0; db < kNdb; ++db)
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2) {
+                adk[db][kb2] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                adv[db][kb2] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+
+        const int nqt = (Nq + kQT - 1) / kQT;
+        // Causal: key j is seen by queries i >= j - off only, so tiles start at
+        // the block's (the wave's) first such query. Keys at or past Lk are
+        // padding: a block (a wave) made of them runs no tile and stores zeros.
+        auto first_tile = [&](int key0) __attribute__((always_inline)) {
+            if (key0 >= Lk) return nqt;
+            return CAUSAL ? min(nqt, max(0, key0 - doff) / kQT) : 0;
+        };
+        const int first = first_tile(k0);
+        const int my_first = first_tile(kw0);
+
+        // L and D of tile u through registers of wave 0 (lanes 0-31: L, 32-63:
+        // D), loaded with the tile's DMA and written to LDS (L scaled to base 2)
+        // after the next tile's compute.
+        float ld_reg = 0.f;
+        auto fetch_ld = [&](int u) __attribute__((always_inline)) {
+            if (wave == 0) {
+                const int q = min(u * kQT + (lane & 31), Nq - 1);
+                ld_reg = lane < 32 ? L[q] : Dv[q];
+            }
+        };
+        auto put_ld = [&](int buf) __attribute__((always_inline)) {
+            if (wave == 0) ld_lds[buf][lane] = lane < 32 ? ld_reg * kLog2e : ld_reg;
+        };
+        Stage16<kQT, false> slots;                 // Q and dO tiles share the offsets
+        slots.init(wave, lane);
+        auto stage = [&](int u, uint16_t* qd, uint16_t* od) __attribute__((always_inline)) {
+            const int q0 = u * kQT;                // < Nq
+            const int valid = min(Nq - q0, kQT);
+            slots.stage(Q + (size_t)q0 * kD, valid, qd, wave);
+            slots.stage(dO + (size_t)q0 * kD, valid, od, wave);
+        };
+
+        // One tile in phases with their own live registers (sched_barrier
+        // between them): S = Q K^T, P, dV^T += dO^T P, dP = dO V^T, dS,
+        // dK^T += Q^T dS.
+        auto compute = [&](int u, const uint16_t* qt, const uint16_t* ot, int buf) __attribute__((always_inline)) {
+            constexpr int LEAD = 2;                // operand prefetch depth (register budget: 256 VGPRs)
+            const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+            // S: s[qb][kb2], lane (n, g): queries 8g + 4qb + e (e = 0..3) of the tile, key 16kb2 + n.
+            f32x4_t s[2][2];
+            op_stream<2 * kNkc, LEAD>([&](int i) { return a_row(qt, i & 1, i >> 1); },
+                                        [&](int i, V8 a) {
+                                            const int qb = i & 1, kc = i >> 1;
+#pragma unroll
+                                            for (int kb2 = 0; kb2 < 2; ++kb2)
+                                                s[qb][kb2] = E::mfma16(a, kf[kb2][kc], kc == 0 ? zero : s[qb][kb2]);
+                                        });
+            const int q0 = u * kQT;
+            const bool edge = q0 + kQT > Nq || kw0 + 32 > Lk || (CAUSAL && q0 + doff < kw0 + 31);
+            // P in place (fp32, kept for dS), then the mask of an edge tile in one branch.
+            const f32x4_t la = *(const f32x4_t*)&ld_lds[buf][8 * g];
+            const f32x4_t lb = *(const f32x4_t*)&ld_lds[buf][8 * g + 4];
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        s[qb][kb2][e] = exp2_hw(__builtin_fmaf(s[qb][kb2][e], scale2, -(qb ? lb[e] : la[e])));
+            if (edge) {
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int q = q0 + 8 * g + 4 * qb + e;
+                            const int key = kw0 + 16 * kb2 + n;
+                            if (q >= Nq || key >= Lk || (CAUSAL && q + doff < key)) s[qb][kb2][e] = 0.f;
+                        }
+            }
+            // P^T of the 32-query step, B operand of dV^T += dO^T P: queries 8g .. 8g+7 of key 16kb2 + n.
+            V8 pf[2];
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2) {
+                u32x4_t w;
+                w[0] = E::pack2(s[0][kb2][0], s[0][kb2][1]);
+                w[1] = E::pack2(s[0][kb2][2], s[0][kb2][3]);
+                w[2] = E::pack2(s[1][kb2][0], s[1][kb2][1]);
+                w[3] = E::pack2(s[1][kb2][2], s[1][kb2][3]);
+                pf[kb2] = __builtin_bit_cast(V8, w);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            op_stream<kNdb, LEAD>([&](int db) { return a_tr(ot, db); },
+                                    [&](int db, V8 a) {
+#pragma unroll
+                                        for (int kb2 = 0; kb2 < 2; ++kb2)
+                                            adv[db][kb2] = E::mfma16(a, pf[kb2], adv[db][kb2]);
+                                    });
+            // dP: both operands from LDS (the dO tile and the block's V rows),
+            // the two A and the two B operands of a d step read one step ahead.
+            f32x4_t dp[2][2];
+            struct Ops { V8 a[2], b[2]; };
+            op_stream<kNkc, 1>([&](int kc) {
+                                     Ops o;
+                                     o.a[0] = a_row(ot, 0, kc);
+                                     o.a[1] = a_row(ot, 1, kc);
+                                     o.b[0] = b_v(0, kc);
+                                     o.b[1] = b_v(1, kc);
+                                     return o;
+                                 },
+                                 [&](int kc, const Ops& o) {
+#pragma unroll
+                                     for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                                         for (int kb2 = 0; kb2 < 2; ++kb2)
+                                             dp[qb][kb2] = E::mfma16(o.a[qb], o.b[kb2], kc == 0 ? zero : dp[qb][kb2]);
+                                 });
+            // dS = P (dP - D), packed like P.
+            const f32x4_t da = *(const f32x4_t*)&ld_lds[buf][kQT + 8 * g];
+            const f32x4_t dbv = *(const f32x4_t*)&ld_lds[buf][kQT + 8 * g + 4];
+            V8 dsf[2];
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2) {
+                float ds[2][4];
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) ds[qb][e] = s[qb][kb2][e] * (dp[qb][kb2][e] - (qb ? dbv[e] : da[e]));
+                u32x4_t x;
+                x[0] = E::pack2(ds[0][0], ds[0][1]);
+                x[1] = E::pack2(ds[0][2], ds[0][3]);
+                x[2] = E::pack2(ds[1][0], ds[1][1]);
+                x[3] = E::pack2(ds[1][2], ds[1][3]);
+                dsf[kb2] = __builtin_bit_cast(V8, x);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            op_stream<kNdb, LEAD>([&](int db) { return a_tr(qt, db); },
+                                    [&](int db, V8 a) {
+#pragma unroll
+                                        for (int kb2 = 0; kb2 < 2; ++kb2)
+                                            adk[db][kb2] = E::mfma16(a, dsf[kb2], adk[db][kb2]);
+                                    });
+        };
+
+        // Prologue: the block's V rows (zeros past Lk) and the first tile.
+        {
+            Stage16<BM_BWD, true> vslots;
+            vslots.init(wave, lane);
+            vslots.stage(Vg + ((size_t)bh * Nk + k0) * kD, max(0, min(Lk - k0, BM_BWD)), v_blk, wave);
+        }
+        if (first < nqt) {
+            stage(first, q_lds0, o_lds0);
+            fetch_ld(first);
+            put_ld(0);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        // Tile first + 2i in buffer 0, first + 2i + 1 in buffer 1.
+        for (int u = first; u < nqt; u += 2) {
+            // Alternating priorities (two workgroups per CU).
+            if ((((u - first) >> 1) + blockIdx.x) & 1) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+            if (u + 1 < nqt) {
+                stage(u + 1, q_lds1, o_lds1);
+                fetch_ld(u + 1);
+            }
+            if (u >= my_first) compute(u, q_lds0, o_lds0, 0);
+            if (u + 1 < nqt) put_ld(1);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (u + 1 >= nqt) break;
+            if (u + 2 < nqt) {
+                stage(u + 2, q_lds0, o_lds0);
+                fetch_ld(u + 2);
+            }
+            if (u + 1 >= my_first) compute(u + 1, q_lds1, o_lds1, 1);
+            if (u + 2 < nqt) put_ld(0);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
+
+        // The last barrier above ended every read of the Q / dO tiles and of the
+        // V block: each wave stages its dK rows in one tile buffer and its dV rows
+        // in its own quarter of the V block. Rows past Nk are not stored.
+        uint16_t* const kst = wave == 0 ? q_lds0 : wave == 1 ? q_lds1 : wave == 2 ? o_lds0 : o_lds1;
+        store_rows16<T>(dKg + ((size_t)bh * Nk + kw0) * kD, Nk - kw0, adk, scale, kst, lane);
+        store_rows16<T>(dVg + ((size_t)bh * Nk + kw0) * kD, Nk - kw0, adv, 1.0f, v_blk + wave * 32 * kD, lane);
+
+        // The next block's loads reuse the LDS buffers.
+        if constexpr (PERSIST) __syncthreads();
+    }
+}
+
+template <typename T>
+static hipError_t launch_dkdv16_t(const BwdArgs& a, float scale2, bool paired) {
+    const int n_bh = a.B * a.H;
+    const int nkb = (a.Nk + BM_BWD - 1) / BM_BWD;
+    int grid = 0;
+    if (paired) {
+        int cus = 0, per_cu = 0;
+        hipError_t e = device_cu_count(&cus);
+        if (e != hipSuccess) return e;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(bwd_dkdv16_kernel<T, true>), kKvThreads, 0);
+        if (e != hipSuccess) return e;
+        grid = paired_schedule_grid(cus * per_cu, n_bh, nkb);
+    }
+    const bool persist = grid > 0;
+    if (!persist) grid = n_bh * nkb;
+    auto kern = persist ? bwd_dkdv16_kernel<T, true> : bwd_dkdv16_kernel<T, false>;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kKvThreads), 0, a.stream,
+                       (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
+                       (const uint16_t*)a.dO, a.LSE, a.Dvec, (uint16_t*)a.dK, (uint16_t*)a.dV, a.kv_lens,
+                       a.H, a.Nq, a.Nk, nkb, a.scale, scale2, a.causal, n_bh);
+    return hipGetLastError();
+}
+
+hipError_t launch_dkdv16(const BwdArgs& a, float scale2, bool paired) {
+    return a.f16 ? launch_dkdv16_t<_Float16>(a, scale2, paired) : launch_dkdv16_t<__bf16>(a, scale2, paired);
+}
+
+}  // namespace fa
