@@ -8,6 +8,9 @@
 //     dV = P^T dO,  dK = scale dS^T Q                  (bwd_dkdv_kernel)
 // Exponentials are base 2 (scale and L multiplied by log2 e).
 //
+// This file holds the D = 64 kernels; D = 128 runs on the 16x16x32 MFMA in
+// fa_bwd16.hip, with the same structure and its own operand layouts.
+//
 // gfx950 mapping (own design, on the forward kernel's MFMA layouts):
 //   * bf16 or fp16 inputs (Elem<T>: MFMA, transpose read, packing).
 //   * Both product kernels use v_mfma_f32_32x32x16_bf16 (_f16) with 4 waves x 32
@@ -46,7 +49,6 @@ namespace {
 constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = 64 * kBwdWaves;
 constexpr int kBT = 32;                    // rows per streamed tile
-constexpr int kDqLead = 4;                 // operand prefetch depth of the dQ kernel (D = 128)
 static_assert(BM_BWD == 32 * kBwdWaves, "32 rows per wave");
 
 #define LDS_AS __attribute__((address_space(3)))
@@ -352,25 +354,13 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
             slots.stage(V + (size_t)kv0 * D, valid, vd, wave);
         };
         auto compute = [&](int t, const uint16_t* kt, const uint16_t* vt) __attribute__((always_inline)) {
-            // S^T = K Q^T and dP^T = V dO^T for 32 keys x this wave's 32 queries.
-            // D = 128: alternating, each LDS operand read a bounded 4 MFMAs ahead
-            // (+2.5-3.3% on the backward over the compiler's own order, which
-            // keeps one pair of reads ahead); D = 64 keeps the compiler's order
-            // (the ring measured 1.4% slower there).
+            // S^T = K Q^T and dP^T = V dO^T for 32 keys x this wave's 32 queries
+            // (the compiler's order: a bounded operand ring measured 1.4% slower).
             f32x16_t s = {}, dp = {};
-            if constexpr (D == 128) {
-                mfma_stream<2 * NKK, kDqLead>(
-                    [&](int i) { return row_operand<T, D>(i % 2 ? vt : kt, off, i / 2); },
-                    [&](int i, V8 a) {
-                        if (i % 2) dp = Elem<T>::mfma(a, dof[i / 2], dp);
-                        else s = Elem<T>::mfma(a, qf[i / 2], s);
-                    });
-            } else {
     #pragma unroll
-                for (int kk = 0; kk < NKK; ++kk) {
-                    s = Elem<T>::mfma(row_operand<T, D>(kt, off, kk), qf[kk], s);
-                    dp = Elem<T>::mfma(row_operand<T, D>(vt, off, kk), dof[kk], dp);
-                }
+            for (int kk = 0; kk < NKK; ++kk) {
+                s = Elem<T>::mfma(row_operand<T, D>(kt, off, kk), qf[kk], s);
+                dp = Elem<T>::mfma(row_operand<T, D>(vt, off, kk), dof[kk], dp);
             }
             const int kv0 = t * kBT;
             const bool edge = kv0 + kBT > Lk || (CAUSAL && kv0 + kBT - 1 > wrow0 + doff);
@@ -404,16 +394,11 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
                 dsf[tt] = __builtin_bit_cast(V8, w);
             }
             // dQ^T += K^T dS^T.
-            if constexpr (D == 128) {
-                mfma_stream<2 * NDB, kDqLead>([&](int i) { return tr_operand<T, D>(kt, off, i / NDB, i % NDB); },
-                                              [&](int i, V8 a) { acc[i % NDB] = Elem<T>::mfma(a, dsf[i / NDB], acc[i % NDB]); });
-            } else {
     #pragma unroll
-                for (int tt = 0; tt < 2; ++tt)
+            for (int tt = 0; tt < 2; ++tt)
     #pragma unroll
-                    for (int db = 0; db < NDB; ++db)
-                        acc[db] = Elem<T>::mfma(tr_operand<T, D>(kt, off, tt, db), dsf[tt], acc[db]);
-            }
+                for (int db = 0; db < NDB; ++db)
+                    acc[db] = Elem<T>::mfma(tr_operand<T, D>(kt, off, tt, db), dsf[tt], acc[db]);
         };
 
         if (ntiles > 0) stage(0, k_lds0, v_lds0);
@@ -447,240 +432,6 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__
         // The next block's loads reuse the LDS buffers.
         if constexpr (PERSIST) __syncthreads();
     }
-}
-
-// dQ (and D) for 256 query rows of one (batch, head) with D = 128, on the
-// forward kernel's ping-pong: 8 waves x 32 rows, one workgroup per CU. Every
-// wave alternates
-//     an MFMA step M(t):  dQ^T += K(t-1)^T dS^T(t-1), then S^T(t) = K(t) Q^T
-//                         and dP^T(t) = V(t) dO^T (24 MFMAs), and
-//     a VALU step V(t):   P(t) = exp2(S scale - L), the mask, dS(t) = P (dP - D)
-//                         rounded to the B operand of the next dQ products,
-// separated by workgroup barriers; waves 4-7 run one step behind waves 0-3,
-// so on every SIMD one wave feeds the matrix core while the other runs the
-// VALU step. Here the MFMA step is the longer one (the forward's is the
-// softmax step).
-// Tiles of 32 keys: K(t) in k buffer t % 3 (it is read by M(t) and M(t+1)),
-// V(t) in v buffer t % 2. Waves 0-3 load tile t+1 during their V(t), which runs
-// beside waves 4-7's M(t) (reading K(t), V(t), K(t-1)); the buffers it fills
-// held K(t-2) and V(t-1), last read in waves 4-7's M(t-1). The loading waves
-// wait for their loads at the end of V(t), and the barrier after it publishes
-// the tile before waves 0-3's M(t+1).
-constexpr int kDqPpWaves = 8;
-constexpr int kDqPpThreads = 64 * kDqPpWaves;
-constexpr int kDqPpRows = 32 * kDqPpWaves;
-
-template <typename T, int D>
-__global__ __launch_bounds__(kDqPpThreads, 1)
-void bwd_dq_pp_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
-                      const uint16_t* __restrict__ Vg, const uint16_t* __restrict__ Og,
-                      const uint16_t* __restrict__ dOg, const float* __restrict__ LSEg, float* __restrict__ Dg,
-                      uint16_t* __restrict__ dQg, const int* __restrict__ kv_lens, int H, int Nq, int Nk,
-                      int nqb, float scale, float scale2, int causal) {
-    using V8 = typename Elem<T>::v8;
-    constexpr int NKK = D / 16, NDB = D / 32;
-    constexpr int TILE = kBT * D;
-    constexpr int LEAD = 4;                    // MFMAs of operand prefetch in the MFMA step
-    const bool CAUSAL = causal != kCausalNone;
-
-    // Three K and two V tile buffers; at the end each wave stages its 32 dQ
-    // rows (one tile's size) here too.
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[kDqPpWaves * TILE];
-    static_assert(kDqPpWaves >= 5, "the staging area holds the five tile buffers");
-
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63;
-    const int j = lane & 31;
-    const int h = lane >> 5;
-    const bool loader = wave < kDqPpWaves / 2;  // waves 0-3, one per SIMD
-
-    const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
-    const int bh = logical / nqb;
-    int qb = logical - bh * nqb;
-    if (CAUSAL) qb = nqb - 1 - qb;             // longest rows first
-    const int q0 = qb * kDqPpRows;
-    const int wrow0 = q0 + wave * 32;
-    const int qrow = wrow0 + j;
-    const bool qvalid = qrow < Nq;
-
-    const uint16_t* K = Kg + (size_t)bh * Nk * D;
-    const uint16_t* V = Vg + (size_t)bh * Nk * D;
-    const int Lk = real_keys(kv_lens, bh / H, Nk);
-    const int doff = causal == kCausalBottomRight ? Lk - Nq : 0;   // key j visible from query i iff j <= i + doff
-
-    int kend = Lk;
-    if (CAUSAL) kend = max(0, min(Lk, min(q0 + kDqPpRows, Nq) + doff));
-    const int ntiles = (kend + kBT - 1) / kBT;
-    const int wlast = wrow0 + 31 + doff;        // last key the wave's last row may see
-    const int my_tiles = CAUSAL ? (wlast < 0 ? 0 : min(ntiles, wlast / kBT + 1)) : ntiles;
-
-    StageSlots<D, kBT> slots;                  // the four loading waves share a tile's chunks
-    slots.init(wave & 3, lane);
-    auto stage = [&](int t, uint16_t* kd, uint16_t* vd) __attribute__((always_inline)) {
-        const int kv0 = t * kBT;               // < kend <= Lk
-        const int valid = min(Lk - kv0, kBT);
-        slots.stage(K + (size_t)kv0 * D, valid, kd, wave & 3);
-        slots.stage(V + (size_t)kv0 * D, valid, vd, wave & 3);
-    };
-
-    // Buffers at constant offsets (the loop below is unrolled over six tiles,
-    // the period of t % 3 and t % 2), so every operand read takes its
-    // buffer's base in the instruction's offset field.
-    uint16_t* const k0 = lds;
-    uint16_t* const k1 = lds + TILE;
-    uint16_t* const k2 = lds + 2 * TILE;
-    uint16_t* const v0 = lds + 3 * TILE;
-    uint16_t* const v1 = lds + 4 * TILE;
-    // Tile 0's loads go out first, ahead of the 96 KB of Q, dO and O rows
-    // each workgroup reads next (those rows are the launch's HBM-bound part).
-    if (loader && ntiles > 0) stage(0, k0, v0);
-    // M(0) runs the dQ products with dS = 0 on K(-1), buffer k2: zero it, as
-    // leftover LDS bits may be NaN (0 x NaN is NaN).
-    static_assert(TILE % (kDqPpThreads * 8) == 0, "whole 16-byte chunks per thread");
-#pragma unroll
-    for (int c = 0; c < TILE / (kDqPpThreads * 8); ++c)
-        *(LDS_AS u32x4_t*)(LDS_AS uint16_t*)(k2 + (c * kDqPpThreads + tid) * 8) = u32x4_t{0u, 0u, 0u, 0u};
-
-    V8 qf[NKK], dof[NKK];
-    load_b_rows<T, D>(Qg + (size_t)bh * Nq * D, qrow, qvalid, h, qf);
-    load_b_rows<T, D>(dOg + (size_t)bh * Nq * D, qrow, qvalid, h, dof);
-    const float l2 = qvalid ? LSEg[(size_t)bh * Nq + qrow] * kLog2e : 0.f;
-    float dr;
-    {
-        V8 of[NKK];
-        load_b_rows<T, D>(Og + (size_t)bh * Nq * D, qrow, qvalid, h, of);
-        float a2[2] = {0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            const u32x4_t a = __builtin_bit_cast(u32x4_t, of[kk]);
-            const u32x4_t b = __builtin_bit_cast(u32x4_t, dof[kk]);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                a2[w & 1] = __builtin_fmaf(Elem<T>::lo(a[w]), Elem<T>::lo(b[w]), a2[w & 1]);
-                a2[w & 1] = __builtin_fmaf(Elem<T>::hi(a[w]), Elem<T>::hi(b[w]), a2[w & 1]);
-            }
-        }
-        dr = sum_xor32(a2[0] + a2[1]);
-        if (qvalid && h == 0) Dg[(size_t)bh * Nq + qrow] = dr;
-    }
-
-    TileOffsets<D> off;
-    off.init(lane);
-
-    f32x16_t acc[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-
-    f32x16_t s, dp;                            // S^T(t), dP^T(t): from M(t) to V(t)
-    V8 dsf[2];                                 // dS^T(t) as B operands: from V(t) to M(t+1)
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) dsf[tt] = __builtin_bit_cast(V8, u32x4_t{0u, 0u, 0u, 0u});
-
-    // kp: K(t-1), kc: K(t), vc: V(t).
-    auto step_m = [&](int t, const uint16_t* kp, const uint16_t* kc, const uint16_t* vc) __attribute__((always_inline)) {
-        __builtin_amdgcn_s_setprio(1);
-        const bool do_dq = t >= 1 && t - 1 < my_tiles;
-        const bool do_sdp = t < my_tiles;
-        constexpr int NQ = 2 * NDB;            // dQ products
-        constexpr int NSD = 2 * NKK;           // S and dP products, alternating
-        const f32x16_t zero = {};
-        // One stream for both parts whenever either is due (separate streams
-        // for the parts alone spill: the branches' live sets do not fit 256
-        // VGPRs together). Running both changes no result: in M(0) dS is zero
-        // and so is K(-1)'s buffer, so the dQ products add exact zeros, and in
-        // the step after a wave's last tile the S and dP products read
-        // in-bounds buffers and are never used.
-        if (do_dq || do_sdp) {
-            mfma_stream<NQ + NSD, LEAD>(
-                [&](int i) {
-                    return i < NQ ? tr_operand<T, D>(kp, off, i / NDB, i % NDB)
-                                  : row_operand<T, D>((i - NQ) % 2 ? vc : kc, off, (i - NQ) / 2);
-                },
-                [&](int i, V8 a) {
-                    if (i < NQ) {
-                        acc[i % NDB] = Elem<T>::mfma(a, dsf[i / NDB], acc[i % NDB]);
-                    } else {
-                        const int k = i - NQ;
-                        if (k % 2) dp = Elem<T>::mfma(a, dof[k / 2], k < 2 ? zero : dp);
-                        else s = Elem<T>::mfma(a, qf[k / 2], k < 2 ? zero : s);
-                    }
-                });
-        }
-        __builtin_amdgcn_s_setprio(0);
-    };
-    auto step_v = [&](int t) __attribute__((always_inline)) {
-        if (t >= my_tiles) return;
-        const int kv0 = t * kBT;
-        const bool edge = kv0 + kBT > Lk || (CAUSAL && kv0 + kBT - 1 > wrow0 + doff);
-        // P in place (register r is key 16*(r/8) + 8*h + r%8 of the tile), then
-        // the mask of an edge tile in one branch.
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = exp2_hw(__builtin_fmaf(s[r], scale2, -l2));
-        if (edge) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = kv0 + (r / 8) * 16 + h * 8 + r % 8;
-                if (key >= Lk || (CAUSAL && key > qrow + doff)) s[r] = 0.f;
-            }
-        }
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            float ds[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ds[e] = s[tt * 8 + e] * (dp[tt * 8 + e] - dr);
-            u32x4_t w;
-            w[0] = Elem<T>::pack2(ds[0], ds[1]);
-            w[1] = Elem<T>::pack2(ds[2], ds[3]);
-            w[2] = Elem<T>::pack2(ds[4], ds[5]);
-            w[3] = Elem<T>::pack2(ds[6], ds[7]);
-            dsf[tt] = __builtin_bit_cast(V8, w);
-        }
-    };
-
-    // Steps M(t), V(t) of one tile; tile t+1 goes to kn and vn. The barrier
-    // between the two steps guards no LDS data (it keeps the groups a step
-    // apart), so it is a plain s_barrier; the one after V(t) publishes the
-    // loads of tile t+1.
-    auto tile_steps = [&](int t, const uint16_t* kp, const uint16_t* kc, const uint16_t* vc, uint16_t* kn,
-                          uint16_t* vn) __attribute__((always_inline)) {
-        step_m(t, kp, kc, vc);
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        if (loader && t + 1 < ntiles) stage(t + 1, kn, vn);
-        step_v(t);
-        lds_dma_wait_all();
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-    };
-
-    lds_dma_wait_all();
-    __syncthreads();
-    if (!loader) __builtin_amdgcn_s_barrier();
-    // t = 0 .. ntiles (M(ntiles) is the last dQ product, V(ntiles) is empty);
-    // K(t) in k[t % 3], V(t) in v[t % 2].
-    for (int t = 0; t <= ntiles; t += 6) {
-        tile_steps(t, k2, k0, v0, k1, v1);
-        if (t + 1 > ntiles) break;
-        tile_steps(t + 1, k0, k1, v1, k2, v0);
-        if (t + 2 > ntiles) break;
-        tile_steps(t + 2, k1, k2, v0, k0, v1);
-        if (t + 3 > ntiles) break;
-        tile_steps(t + 3, k2, k0, v1, k1, v0);
-        if (t + 4 > ntiles) break;
-        tile_steps(t + 4, k0, k1, v0, k2, v1);
-        if (t + 5 > ntiles) break;
-        tile_steps(t + 5, k1, k2, v1, k0, v0);
-    }
-    if (loader) __builtin_amdgcn_s_barrier();
-
-    // Every wave has passed the last barrier of both groups: no tile buffer is
-    // read again, and each wave stages its dQ rows in its own tile-sized slot.
-    store_rows_staged<T, D>(dQg + ((size_t)bh * Nq + wrow0) * D, Nq - wrow0, acc, scale, lds + wave * TILE, lane);
 }
 
 // dK and dV for 128 keys of one (batch, head), streaming Q, dO, L and D tiles.
@@ -961,41 +712,25 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
     // padding), where a block's cost is linear in its index, so that the
     // paired blocks cost the same.
     const bool paired = a.causal != kCausalNone && !a.kv_lens && a.Nq == a.Nk;
-    // dQ (and D): the ping-pong kernel for non-causal D = 128; the 4-wave
-    // kernel otherwise (causal: a 256-row block leaves more waves idle along
-    // the diagonal, measured 2% slower on causal 4x32x4096).
     if (a.Nq > 0) {
-        bool pp = false;
-        if constexpr (D == 128) pp = a.causal == kCausalNone;
-        if (pp) {
-            if constexpr (D == 128) {
-                const int nqb = (a.Nq + kDqPpRows - 1) / kDqPpRows;
-                hipLaunchKernelGGL((bwd_dq_pp_kernel<T, D>), dim3(a.B * a.H * nqb), dim3(kDqPpThreads), 0,
-                                   a.stream, (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
-                                   (const uint16_t*)a.O, (const uint16_t*)a.dO, a.LSE, a.Dvec, (uint16_t*)a.dQ,
-                                   a.kv_lens, a.H, a.Nq, a.Nk, nqb, a.scale, scale2, a.causal);
-            }
-        } else {
-            const int nqb = (a.Nq + BM_BWD - 1) / BM_BWD;
-            int grid = 0;
-            if (paired) {
-                const hipError_t e = persistent_grid(bwd_dq_kernel<T, D, true>, n_bh, nqb, &grid);
-                if (e != hipSuccess) return e;
-            }
-            const bool persist = grid > 0;
-            if (!persist) grid = n_bh * nqb;
-            auto kern = persist ? bwd_dq_kernel<T, D, true> : bwd_dq_kernel<T, D, false>;
-            hipLaunchKernelGGL(kern, dim3(grid), dim3(kBwdThreads), 0, a.stream,
-                               (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
-                               (const uint16_t*)a.O, (const uint16_t*)a.dO, a.LSE, a.Dvec, (uint16_t*)a.dQ,
-                               a.kv_lens, a.H, a.Nq, a.Nk, nqb, a.scale, scale2, a.causal, n_bh);
+        const int nqb = (a.Nq + BM_BWD - 1) / BM_BWD;
+        int grid = 0;
+        if (paired) {
+            const hipError_t e = persistent_grid(bwd_dq_kernel<T, D, true>, n_bh, nqb, &grid);
+            if (e != hipSuccess) return e;
         }
-        hipError_t e = hipGetLastError();
+        const bool persist = grid > 0;
+        if (!persist) grid = n_bh * nqb;
+        auto kern = persist ? bwd_dq_kernel<T, D, true> : bwd_dq_kernel<T, D, false>;
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(kBwdThreads), 0, a.stream,
+                           (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V,
+                           (const uint16_t*)a.O, (const uint16_t*)a.dO, a.LSE, a.Dvec, (uint16_t*)a.dQ,
+                           a.kv_lens, a.H, a.Nq, a.Nk, nqb, a.scale, scale2, a.causal, n_bh);
+        const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     // With Nq = 0 the dK/dV kernel stages only V, runs no query tile and
-    // stores zeros. D = 128 runs on the 16x16x32 MFMA (fa_bwd16.hip).
-    if constexpr (D == 128) return launch_dkdv16(a, scale2, paired);
+    // stores zeros.
     const int nkb = (a.Nk + BM_BWD - 1) / BM_BWD;
     int grid = 0;
     if (paired) {
@@ -1013,8 +748,9 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
 }
 
 hipError_t launch_bwd(const BwdArgs& a) {
-    if (a.f16) return a.D == 128 ? launch_bwd_d<_Float16, 128>(a) : launch_bwd_d<_Float16, 64>(a);
-    return a.D == 128 ? launch_bwd_d<__bf16, 128>(a) : launch_bwd_d<__bf16, 64>(a);
+    // D = 128 runs on the 16x16x32 MFMA (fa_bwd16.hip).
+    if (a.D == 128) return launch_bwd16(a);
+    return a.f16 ? launch_bwd_d<_Float16, 64>(a) : launch_bwd_d<__bf16, 64>(a);
 }
 
 }  // namespace fa

@@ -1,27 +1,29 @@
-// dK and dV of the backward pass with recompute for D = 128 on the 16x16x32
-// MFMA (v_mfma_f32_16x16x32_bf16 / _f16), the products of the "Backward with
-// recompute" exercise and section 11.9 of the ML compiler page that fall to
-// the key side:
+// Backward pass with recompute for D = 128 on the 16x16x32 MFMA
+// (v_mfma_f32_16x16x32_bf16 / _f16): the products of the "Backward with
+// recompute" exercise and section 11.9 of the ML compiler page,
+//     D_i = sum_d dO[i,d] O[i,d]                      (bwd_dq16_kernel, stored)
 //     P = exp(scale Q K^T - L),  dP = dO V^T,  dS = P * (dP - D)
-//     dV = P^T dO,  dK = scale dS^T Q
-// (base-2 exponentials, L and scale multiplied by log2 e; D = rowsum(dO * O)
-// comes from the dQ kernel). It does what bwd_dkdv_kernel of fa_bwd.hip does
-// for D = 64 with the 32x32x16 MFMA, on the 16x16x32 shape: on random
-// operands that shape holds the chip's power limit at a higher engine clock
-// for the same work.
+//     dQ = scale dS K                                 (bwd_dq16_kernel)
+//     dV = P^T dO,  dK = scale dS^T Q                 (bwd_dkdv16_kernel)
+// with base-2 exponentials (L and scale multiplied by log2 e). The kernels
+// keep the structure of fa_bwd.hip's D = 64 kernels (4 waves x 32 rows, the
+// other operand streamed through LDS in 32-row tiles, masks, persistent
+// causal launches) on the 16x16x32 shape: on random operands that shape holds
+// the chip's power limit at a higher engine clock for the same work.
 //
 // 16x16x32 layouts (lane l, n = l % 16, g = l / 16): A lane holds row n,
 // k = 8g..8g+7; B lane holds k = 8g..8g+7 of column n; the accumulator lane
-// holds rows 4g..4g+3 of column n. A wave owns 32 keys (two column blocks kb2
-// of 16) and streams query tiles of 32 rows (two row blocks qb of 16):
-//   * S = Q K^T and dP = dO V^T: A = the tile's rows, B = K (registers) or V
-//     (the block's rows in LDS). Row m of block qb reads tile row
-//     8(m/4) + 4qb + m%4, so the lane ends with queries 8g + 4qb + 0..3 of its
-//     key: over both blocks, the eight queries 8g..8g+7 in order, which
-//     rounded to 16 bits is the B operand of the 32-query step of
-//     dV^T += dO^T P and dK^T += Q^T dS. P and dS never leave registers.
-//   * dO^T and Q^T (A of those products: row d = 16db + n, queries 8g..8g+7)
-//     are two ds_read_b64_tr_b16 of 4 rows each from the same tiles.
+// holds rows 4g..4g+3 of column n. A wave's 32 own rows (keys in the dK/dV
+// kernel, queries in the dQ kernel) are two column blocks of 16, and a 32-row
+// tile of the streamed side is two row blocks of 16:
+//   * The first products (S and dP, or their transposes) take the tile's rows
+//     as A, with row m of block b reading tile row 8(m/4) + 4b + m%4, so the
+//     lane ends with tile rows 8g + 4b + 0..3 of its own row: over both
+//     blocks, the eight rows 8g..8g+7 in order, which rounded to 16 bits is
+//     the B operand of the 32-row step of the products that follow (dV, dK or
+//     dQ). P and dS never leave registers.
+//   * The A operands of those products (the tile transposed: row d = 16db + n,
+//     tile rows 8g..8g+7) are two ds_read_b64_tr_b16 of 4 rows each.
 //   * Tiles are staged once and read both ways: the 16-byte chunk swizzle
 //     2(row % 4) | 8(row bit 3) | (row bit 4) is free of bank conflicts for
 //     the row reads (16 lanes, 16 rows, one chunk) and the transpose reads (32
@@ -451,6 +453,249 @@ void bwd_dkdv16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restri
     }
 }
 
+// dQ (and D) for 128 query rows of one (batch, head): 4 waves x 32 queries,
+// two workgroups per CU, K and V streamed through LDS in 32-key tiles
+// (double-buffered, one barrier per tile), with the dK/dV kernel's 16x16x32
+// layouts on the query side. A wave's 32 queries are two column blocks qb of
+// 16 (Q and dO in registers as B operands); a tile is two row blocks kb of 16
+// keys whose A rows are permuted (row m of block kb reads key 8(m/4) + 4kb +
+// m%4), so the lane ends with keys 8g + 4kb + 0..3 of its query and dS^T packs
+// straight into the B operand of dQ^T += K^T dS^T, whose K^T operand is two
+// transpose reads of the same tile.
+template <typename T, bool PERSIST>
+__global__ __launch_bounds__(kKvThreads, 2)
+void bwd_dq16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
+                     const uint16_t* __restrict__ Vg, const uint16_t* __restrict__ Og,
+                     const uint16_t* __restrict__ dOg, const float* __restrict__ LSEg, float* __restrict__ Dg,
+                     uint16_t* __restrict__ dQg, const int* __restrict__ kv_lens, int H, int Nq, int Nk,
+                     int nqb, float scale, float scale2, int causal, int n_bh) {
+    using E = Elem<T>;
+    using V8 = typename E::v8;
+    using V4 = typename E::v4;
+    constexpr int LEAD = 4;                    // operand prefetch depth of the product streams
+    const bool CAUSAL = causal != kCausalNone;
+
+    __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[kQTile];
+    __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[kQTile];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[kQTile];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[kQTile];
+
+    // One query block per workgroup or, in a persistent launch, the paired
+    // static schedule of bwd_dq_kernel (blocks nqb - 1 - r and r of a head at
+    // equal cost, contiguous pair ranges per XCD, taken in turn).
+    const int npair = (nqb + 1) / 2;
+    const int xcd = blockIdx.x & 7;
+    const int per_xcd = gridDim.x >> 3;
+    const long long all_pairs = (long long)n_bh * npair;
+    const int p_lo = (int)(all_pairs * xcd / 8), p_hi = (int)(all_pairs * (xcd + 1) / 8);
+    for (int wi = 0;; ++wi) {
+        int bh, qb0;
+        if constexpr (!PERSIST) {
+            if (wi > 0) break;
+            const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
+            bh = logical / nqb;
+            qb0 = logical - bh * nqb;
+            if (CAUSAL) qb0 = nqb - 1 - qb0;   // longest rows first
+        } else {
+            const int p = p_lo + (int)(blockIdx.x >> 3) + (wi >> 1) * per_xcd;
+            if (p >= p_hi) break;
+            bh = p / npair;
+            const int r = p - bh * npair;
+            qb0 = (wi & 1) ? r : nqb - 1 - r;
+            if ((wi & 1) && r == nqb - 1 - r) continue;   // odd count: the middle block is alone
+        }
+        int tid = threadIdx.x;
+        if constexpr (PERSIST) asm volatile("" : "+v"(tid));
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int lane = tid & 63;
+        const int n = lane & 15;
+        const int g = lane >> 4;
+        const int q0 = qb0 * BM_BWD;
+        const int wrow0 = q0 + wave * 32;
+
+        const uint16_t* K = Kg + (size_t)bh * Nk * kD;
+        const uint16_t* V = Vg + (size_t)bh * Nk * kD;
+        const int Lk = real_keys(kv_lens, bh / H, Nk);
+        const int doff = causal == kCausalBottomRight ? Lk - Nq : 0;   // key j visible from query i iff j <= i + doff
+
+        // Q and dO of the wave's queries as B operands: query wrow0 + 16qb + n,
+        // d = 32kc + 8g .. +7 (zero past Nq); D = rowsum(dO * O) of those
+        // queries from the O rows read the same way, over the four lane groups,
+        // written for the dK/dV kernel.
+        V8 qf[2][kNkc], dof[2][kNkc];
+        float l2[2], dr[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const int q = wrow0 + 16 * qb + n;
+            const bool qv = q < Nq;
+            const size_t rowb = ((size_t)bh * Nq + min(q, Nq - 1)) * kD;
+            float a2[2] = {0.f, 0.f};
+#pragma unroll
+            for (int kc = 0; kc < kNkc; ++kc) {
+                u32x4_t wq = *(const u32x4_t*)(Qg + rowb + kc * 32 + g * 8);
+                u32x4_t wd = *(const u32x4_t*)(dOg + rowb + kc * 32 + g * 8);
+                const u32x4_t wo = *(const u32x4_t*)(Og + rowb + kc * 32 + g * 8);
+                if (!qv) wq = wd = u32x4_t{0u, 0u, 0u, 0u};
+                qf[qb][kc] = __builtin_bit_cast(V8, wq);
+                dof[qb][kc] = __builtin_bit_cast(V8, wd);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    a2[w & 1] = __builtin_fmaf(E::lo(wo[w]), E::lo(wd[w]), a2[w & 1]);
+                    a2[w & 1] = __builtin_fmaf(E::hi(wo[w]), E::hi(wd[w]), a2[w & 1]);
+                }
+            }
+            dr[qb] = sum_xor32(sum_xor16(a2[0] + a2[1]));
+            if (qv && g == 0) Dg[(size_t)bh * Nq + q] = dr[qb];
+            l2[qb] = qv ? LSEg[(size_t)bh * Nq + q] * kLog2e : 0.f;
+        }
+
+        // Lane byte offsets of the LDS operand reads (tile bases fold into the
+        // instruction's offset field): rowoff[kc], tile row 8(n/4) + n%4, chunk
+        // 4kc + g (row block 1: +4 rows); troff[db], tile row 8g + n/4, columns
+        // 16db + 4(n%4) .. +3 (second transpose read: +4 rows).
+        uint32_t rowoff[kNkc], troff[kNdb];
+        {
+            const int r = 8 * (n >> 2) + (n & 3);
+            const int q = 8 * g + (n >> 2);
+#pragma unroll
+            for (int kc = 0; kc < kNkc; ++kc) {
+                rowoff[kc] = (uint32_t)(r * kD + ((4 * kc + g) ^ tile_swz(r)) * 8) * 2u;
+                asm volatile("" : "+v"(rowoff[kc]));
+            }
+#pragma unroll
+            for (int db = 0; db < kNdb; ++db) {
+                const int col = 16 * db + 4 * (n & 3);
+                troff[db] = (uint32_t)(q * kD + ((col >> 3) ^ tile_swz(q)) * 8 + (col & 7)) * 2u;
+                asm volatile("" : "+v"(troff[db]));
+            }
+        }
+        auto a_row = [&](const uint16_t* tile, int kb, int kc) __attribute__((always_inline)) {
+            return *(LDS16B const V8*)((LDS16B const char*)(LDS16B const uint16_t*)tile + rowoff[kc] + kb * 1024);
+        };
+        auto a_tr = [&](const uint16_t* tile, int db) __attribute__((always_inline)) {
+            const V4 p0 = E::tr_read((LDS16B V4*)((LDS16B char*)(LDS16B uint16_t*)tile + troff[db]));
+            const V4 p1 = E::tr_read((LDS16B V4*)((LDS16B char*)(LDS16B uint16_t*)tile + troff[db] + 1024));
+            return V8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+        };
+
+        // dQ^T: acc[db][qb], lane (n, g) holds d = 16db + 4g .. +3 of query 16qb + n.
+        f32x4_t acc[kNdb][2];
+#pragma unroll
+        for (int db = 0; db < kNdb; ++db)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) acc[db][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+        int kend = Lk;
+        if (CAUSAL) kend = max(0, min(Lk, min(q0 + BM_BWD, Nq) + doff));
+        const int ntiles = (kend + kQT - 1) / kQT;
+        const int wlast = wrow0 + 31 + doff;        // last key the wave's last row may see
+        const int my_tiles = CAUSAL ? (wlast < 0 ? 0 : min(ntiles, wlast / kQT + 1)) : ntiles;
+
+        Stage16<kQT, false> slots;                 // K and V tiles share the offsets
+        slots.init(wave, lane);
+        auto stage = [&](int t, uint16_t* kd, uint16_t* vd) __attribute__((always_inline)) {
+            const int kv0 = t * kQT;               // < kend <= Lk
+            const int valid = min(Lk - kv0, kQT);
+            slots.stage(K + (size_t)kv0 * kD, valid, kd, wave);
+            slots.stage(V + (size_t)kv0 * kD, valid, vd, wave);
+        };
+        auto compute = [&](int t, const uint16_t* kt, const uint16_t* vt) __attribute__((always_inline)) {
+            const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+            // S^T = K Q^T and dP^T = V dO^T: s[kb][qb], lane (n, g) holds keys
+            // 8g + 4kb + 0..3 of the tile for query 16qb + n; the operands K kb 0,
+            // K kb 1, V kb 0, V kb 1 of each d step in one stream.
+            f32x4_t s[2][2], dp[2][2];
+            op_stream<4 * kNkc, LEAD>([&](int k) { return a_row((k & 2) ? vt : kt, k & 1, k >> 2); },
+                                      [&](int k, V8 a) {
+                                          const int kb = k & 1, kc = k >> 2;
+                                          if (k & 2) {
+#pragma unroll
+                                              for (int qb = 0; qb < 2; ++qb)
+                                                  dp[kb][qb] = E::mfma16(a, dof[qb][kc], kc == 0 ? zero : dp[kb][qb]);
+                                          } else {
+#pragma unroll
+                                              for (int qb = 0; qb < 2; ++qb)
+                                                  s[kb][qb] = E::mfma16(a, qf[qb][kc], kc == 0 ? zero : s[kb][qb]);
+                                          }
+                                      });
+            const int kv0 = t * kQT;
+            const bool edge = kv0 + kQT > Lk || (CAUSAL && kv0 + kQT - 1 > wrow0 + doff);
+            // P in place, then the mask of an edge tile in one branch.
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        s[kb][qb][e] = exp2_hw(__builtin_fmaf(s[kb][qb][e], scale2, -l2[qb]));
+            if (edge) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int key = kv0 + 8 * g + 4 * kb + e;
+                            const int q = wrow0 + 16 * qb + n;
+                            if (key >= Lk || (CAUSAL && key > q + doff)) s[kb][qb][e] = 0.f;
+                        }
+            }
+            // dS^T as B operands: keys 8g .. 8g+7 of query 16qb + n.
+            V8 dsf[2];
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                float ds[2][4];
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) ds[kb][e] = s[kb][qb][e] * (dp[kb][qb][e] - dr[qb]);
+                u32x4_t w;
+                w[0] = E::pack2(ds[0][0], ds[0][1]);
+                w[1] = E::pack2(ds[0][2], ds[0][3]);
+                w[2] = E::pack2(ds[1][0], ds[1][1]);
+                w[3] = E::pack2(ds[1][2], ds[1][3]);
+                dsf[qb] = __builtin_bit_cast(V8, w);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // dQ^T += K^T dS^T.
+            op_stream<kNdb, LEAD>([&](int db) { return a_tr(kt, db); },
+                                  [&](int db, V8 a) {
+#pragma unroll
+                                      for (int qb = 0; qb < 2; ++qb) acc[db][qb] = E::mfma16(a, dsf[qb], acc[db][qb]);
+                                  });
+        };
+
+        if (ntiles > 0) stage(0, k_lds0, v_lds0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        // Tile t in buffer t % 2; the next tile is loaded while t is computed and
+        // published by the barrier that ends the iteration.
+        for (int t = 0; t < ntiles; t += 2) {
+            // Alternating priorities by tile pair and block parity (two
+            // workgroups per CU, as in bwd_dq_kernel).
+            if (((t >> 1) + blockIdx.x) & 1) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+            if (t + 1 < ntiles) stage(t + 1, k_lds1, v_lds1);
+            if (t < my_tiles) compute(t, k_lds0, v_lds0);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (t + 1 >= ntiles) break;
+            if (t + 2 < ntiles) stage(t + 2, k_lds0, v_lds0);
+            if (t + 1 < my_tiles) compute(t + 1, k_lds1, v_lds1);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
+
+        // The last barrier above ended every read of the tile buffers: each wave
+        // stages its dQ rows in one of them.
+        uint16_t* const qst = wave == 0 ? k_lds0 : wave == 1 ? k_lds1 : wave == 2 ? v_lds0 : v_lds1;
+        store_rows16<T>(dQg + ((size_t)bh * Nq + wrow0) * kD, Nq - wrow0, acc, scale, qst, lane);
+
+        // The next block's loads reuse the LDS buffers.
+        if constexpr (PERSIST) __syncthreads();
+    }
+}
+
 template <typename T>
 static hipError_t launch_dkdv16_t(const BwdArgs& a, float scale2, bool paired) {
     const int n_bh = a.B * a.H;
@@ -475,7 +720,42 @@ static hipError_t launch_dkdv16_t(const BwdArgs& a, float scale2, bool paired) {
     return hipGetLastError();
 }
 
-hipError_t launch_dkdv16(const BwdArgs& a, float scale2, bool paired) {
+template <typename T>
+static hipError_t launch_dq16_t(const BwdArgs& a, float scale2, bool paired) {
+    const int n_bh = a.B * a.H;
+    const int nqb = (a.Nq + BM_BWD - 1) / BM_BWD;
+    int grid = 0;
+    if (paired) {
+        int cus = 0, per_cu = 0;
+        hipError_t e = device_cu_count(&cus);
+        if (e != hipSuccess) return e;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(bwd_dq16_kernel<T, true>), kKvThreads, 0);
+        if (e != hipSuccess) return e;
+        grid = paired_schedule_grid(cus * per_cu, n_bh, nqb);
+    }
+    const bool persist = grid > 0;
+    if (!persist) grid = n_bh * nqb;
+    auto kern = persist ? bwd_dq16_kernel<T, true> : bwd_dq16_kernel<T, false>;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kKvThreads), 0, a.stream,
+                       (const uint16_t*)a.Q, (const uint16_t*)a.K, (const uint16_t*)a.V, (const uint16_t*)a.O,
+                       (const uint16_t*)a.dO, a.LSE, a.Dvec, (uint16_t*)a.dQ, a.kv_lens, a.H, a.Nq, a.Nk, nqb,
+                       a.scale, scale2, a.causal, n_bh);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd16(const BwdArgs& a) {
+    const float scale2 = a.scale * kLog2e;
+    // Persistent launches for causal self-attention (Nq = Nk, no key padding),
+    // where a block's cost is linear in its index, so that paired blocks cost
+    // the same.
+    const bool paired = a.causal != kCausalNone && !a.kv_lens && a.Nq == a.Nk;
+    if (a.Nq > 0) {
+        const hipError_t e = a.f16 ? launch_dq16_t<_Float16>(a, scale2, paired) : launch_dq16_t<__bf16>(a, scale2, paired);
+        if (e != hipSuccess) return e;
+    }
+    // With Nq = 0 the dK/dV kernel stages only V, runs no query tile and
+    // stores zeros.
     return a.f16 ? launch_dkdv16_t<_Float16>(a, scale2, paired) : launch_dkdv16_t<__bf16>(a, scale2, paired);
 }
 

@@ -102,9 +102,8 @@ constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
 // device, then cached).
 hipError_t decode_scratch(void** ptr);
 hipError_t launch_bwd(const BwdArgs& a);
-// dK and dV for D = 128 on the 16x16x32 MFMA (fa_bwd16.hip); `paired` asks for the
-// persistent causal schedule where it shares out evenly.
-hipError_t launch_dkdv16(const BwdArgs& a, float scale2, bool paired);
+// The backward for D = 128, on the 16x16x32 MFMA (fa_bwd16.hip).
+hipError_t launch_bwd16(const BwdArgs& a);
 // Compute units of the current device (asked once per device), for the
 // persistent causal launches.
 hipError_t device_cu_count(int* n);
