@@ -78,7 +78,7 @@ LEGS = {
 FWD_FILES = ["fa_fwd_mfma.hip", "fa_fwd_mfma16.hip", "fa_device.h", "fa_internal.h"]
 F32_FILES = ["fa_fwd_f32.hip", "fa_device.h", "fa_internal.h"]
 DEC_FILES = ["fa_decode.hip", "fa_device.h", "fa_internal.h"]
-BWD_FILES = ["fa_bwd.hip", "fa_bwd16.hip", "fa_device.h", "fa_internal.h"]
+BWD_FILES = ["fa_bwd.hip", "fa_device.h", "fa_internal.h"]
 
 
 def _code_only(text):
@@ -337,10 +337,8 @@ def backward_leg(fa, synth, torch, w, steps, warmup):
     leg = {
         "workload": w.name, "ms_per_call": round(ms, 6), "value": round(tf, 3), "unit": "TFLOP/s",
         "algorithmic_flops": flops,
-        # the two kernels of this shape: dQ (and D), then dK/dV; D = 128 on
-        # the 16x16x32 MFMA
-        "roofline": roofline("bwd_dq16_kernel + bwd_dkdv16_kernel" if w.D == 128 else "bwd_dq_kernel + bwd_dkdv_kernel",
-                             "mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s",
+        # the two kernels: dQ (and D), then dK/dV
+        "roofline": roofline("bwd_dq16_kernel + bwd_dkdv16_kernel", "mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s",
                              f"bwd_kernels_{w.name}", digest, True),
     }
     return leg, (q, k, v, do)

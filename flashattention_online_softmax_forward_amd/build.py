@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libfa_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["fa_api.hip", "fa_fwd_mfma.hip", "fa_fwd_mfma16.hip", "fa_fwd_f32.hip", "fa_decode.hip", "fa_bwd.hip", "fa_bwd16.hip",
+SOURCES = ["fa_api.hip", "fa_fwd_mfma.hip", "fa_fwd_mfma16.hip", "fa_fwd_f32.hip", "fa_decode.hip", "fa_bwd.hip",
            "fa_rope.hip"]
 ARCH = "gfx950"
 

@@ -102,8 +102,6 @@ constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
 // device, then cached).
 hipError_t decode_scratch(void** ptr);
 hipError_t launch_bwd(const BwdArgs& a);
-// The backward for D = 128, on the 16x16x32 MFMA (fa_bwd16.hip).
-hipError_t launch_bwd16(const BwdArgs& a);
 // Compute units of the current device (asked once per device), for the
 // persistent causal launches.
 hipError_t device_cu_count(int* n);
