@@ -94,9 +94,9 @@ CASES = [
     (1, 4, 513, 513, 128, True, 3.0),      # scores std ~ 9 (the rescale-stress inputs)
     (1, 2, 1000, 1000, 64, True, 1.0),
     (2, 2, 129, 1025, 128, False, 3.0),
-    # Non-causal D = 128 (the ping-pong kernels, whose two wave groups take
-    # alternate 32-row query tiles): an odd tile count with a ragged second
-    # key block, two tiles the second of one row, two whole tiles.
+    # Non-causal D = 128 with few 32-row tiles: an odd tile count with a
+    # ragged second key block, two tiles the second of one row, two whole
+    # tiles.
     (1, 2, 96, 160, 128, False, 1.0),
     (1, 1, 33, 64, 128, False, 1.0),
     (1, 1, 64, 64, 128, False, 3.0),

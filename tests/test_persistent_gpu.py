@@ -11,7 +11,7 @@ launch. The two must agree bit for bit (every block is the same computation
 whichever workgroup runs it), and sampled heads are also checked against the
 oracle. The shapes are chosen so that the pairs share out evenly over the
 256 CUs (forward, one workgroup per CU) and over 512 slots (backward with
-D = 128, two per CU), including an odd block count, where the middle block
+D = 128, two per CU; 768 with D = 64, three per CU), including an odd block count, where the middle block
 has no partner.
 """
 
@@ -90,6 +90,7 @@ BWD_CASES = [
     # (B, H, N, D, causal): query and key blocks of 128 rows
     (4, 32, 1024, 128, 1),   # 8 blocks per head: four pairs
     (4, 64, 384, 128, 1),    # 3 blocks: pair (2, 0) and block 1 alone
+    (4, 48, 1024, 64, 1),    # D = 64: three workgroups per CU, 768 slots
 ]
 
 
@@ -97,7 +98,7 @@ BWD_CASES = [
 def test_persistent_backward_matches_per_head(fa, case):
     B, H, N, D, causal = case
     print(f"[case] persistent bwd {case}", flush=True)
-    assert pairs_fill(B * H, -(-N // 128), 512)
+    assert pairs_fill(B * H, -(-N // 128), 512 if D == 128 else 768)
     q, k, v = synth.make_qkv(B, H, N, N, D, torch.bfloat16, seed=42)
     do = synth.make_do(B, H, N, D, torch.bfloat16, seed=42)
     qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
