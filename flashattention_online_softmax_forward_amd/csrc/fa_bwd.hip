@@ -167,6 +167,12 @@ __device__ __forceinline__ void op_stream(Op op, Step step) {
 
 }  // namespace
 
+// dK and dV for 128 keys of one (batch, head): 4 waves x 32 keys, K in
+// registers (B operand of S = Q K^T) and the block's V rows in LDS (B operand
+// of dP = dO V^T), Q and dO streamed in 32-row tiles with their L and D
+// values. A tile's phases (S, P, dV, dP, dS, dK) are separated by
+// sched_barrier and read their LDS operands a bounded number of steps ahead,
+// which keeps the D = 128 kernel within 256 VGPRs.
 template <typename T, int D, bool PERSIST>
 __global__ __launch_bounds__(kKvThreads, 2)
 void bwd_dkdv16_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
